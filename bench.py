@@ -1,0 +1,176 @@
+"""Benchmark: tree-structured decode attention, one decode step of one layer.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+
+A step is one tree_attn_decode (partial-attention kernel + log-sum-exp
+reduction) over the whole tree. The default workload is the multi-level
+shared system prompt tree (nodes per level 1/4/16, 2048/512/128 tokens per
+node, 32 q-heads / 32 kv-heads, head_dim 128, bf16, page size 16).
+
+The KV pool is replicated into enough copies (>= 1 GiB together) that each
+timed step reads a copy no cache level holds from the step before: the 256 MB
+Infinity Cache would otherwise serve the whole tree. Inputs are resident in
+HBM before the timed region. Prints one JSON line.
+"""
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "tree-decode attn: µs/step + effective HBM GB/s (unique KV bytes) vs peak"
+
+
+def _cpu_baseline(inst, budget_s=12.0, max_reps=20):
+    """The fp64 oracle, untuned, on the host cores: whole decode steps of the
+    same workload, repeated until ~budget_s of CPU work."""
+    from oracle import tree_attention as oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    times = []
+    t_all = time.perf_counter()
+    while len(times) < max_reps and (time.perf_counter() - t_all) < budget_s:
+        t0 = time.perf_counter()
+        oracle.decode_instance(inst)
+        times.append(time.perf_counter() - t0)
+    med = statistics.median(times)
+    return {
+        "value": round(inst.unique_kv_bytes / med / 1e9, 4),
+        "unit": "GB/s",
+        "us_per_step": round(med * 1e6, 1),
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{len(times)} full decode steps of the same tree (all {inst.n_queries} queries, "
+                  f"fp64 numpy), median",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--copies", type=int, default=0, help="KV pool copies (0 = enough for 1 GiB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: the method runs one layer's decode on one device "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    from tree_structured_shared_amd import Plan
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inst = synth.make_config(args.config)
+    unique = inst.unique_kv_bytes
+    esize = 2 if inst.dtype == torch.bfloat16 else 4
+    pool_bytes = 2 * inst.k_pool.numel() * esize
+    copies = args.copies or max(2, math.ceil((1 << 30) / pool_bytes) + 1)
+
+    # planner host time (tables only, then the full plan with its one upload)
+    t_host = []
+    for _ in range(20):
+        t0 = time.perf_counter()
+        Plan.for_instance(inst, host_only=True).close()
+        t_host.append(time.perf_counter() - t0)
+    t0 = time.perf_counter()
+    plan = Plan.for_instance(inst)
+    t_plan_full = time.perf_counter() - t0
+    P = plan.export("params")
+
+    q = inst.q.to(dev)
+    ks = [inst.k_pool.to(dev) for _ in range(copies)]
+    vs = [inst.v_pool.to(dev) for _ in range(copies)]
+    out = torch.empty((inst.n_queries, inst.n_qheads, inst.head_dim), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    calls = [plan.launcher(q, ks[c], vs[c], out, stream.cuda_stream) for c in range(copies)]
+
+    for s in range(args.warmup):
+        calls[s % copies]()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    plan.timing_enable(K)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        calls[s % copies]()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pm, rm = plan.timing_read(K)
+
+    # warm reference: the same copy every step (Infinity Cache may hold it)
+    plan.timing_enable(K)
+    for s in range(K):
+        calls[0]()
+    torch.cuda.synchronize()
+    pm_w, rm_w = plan.timing_read(K)
+
+    ms_per_step = wall * 1e3 / K
+    part_us = float(np.mean(pm)) * 1e3
+    red_us = float(np.mean(rm)) * 1e3
+    value = unique / (ms_per_step * 1e-3) / 1e9
+    achieved = unique / (part_us * 1e-6) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "frac_of_peak": round(value / HBM_PEAK_GBS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if inst.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": inst.name,
+            "n_nodes": inst.n_nodes,
+            "n_queries": inst.n_queries,
+            "queries_per_leaf": inst.qpl,
+            "n_qheads": inst.n_qheads,
+            "n_kvheads": inst.n_kvheads,
+            "head_dim": inst.head_dim,
+            "page_size": inst.page_size,
+            "unique_kv_bytes": unique,
+            "kv_copies_rotated": copies,
+            "plan": {"groups": int(P[18]), "chunks": int(P[19]), "items": int(P[20]),
+                     "slots": int(P[21]), "workgroups": int(P[20]) * inst.n_kvheads,
+                     "edges_joined": int(plan.export("edges").sum())},
+        },
+        "kernels_us": {"partial_attn": round(part_us, 3), "lse_reduce": round(red_us, 3),
+                       "device_step": round(float(np.mean(pm + rm)) * 1e3, 3),
+                       "partial_attn_warm": round(float(np.mean(pm_w)) * 1e3, 3),
+                       "lse_reduce_warm": round(float(np.mean(rm_w)) * 1e3, 3)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "planner_host_ms": {"tables_median": round(statistics.median(t_host) * 1e3, 3),
+                            "with_upload": round(t_plan_full * 1e3, 3)},
+    }
+    plan.close()
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = _cpu_baseline(inst)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

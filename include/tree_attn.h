@@ -1,0 +1,167 @@
+/*
+ * tree_attn.h -- C ABI of the MI355X tree-structured decode attention library.
+ *
+ * What it computes. Every query token sits at a leaf of a decoding tree whose
+ * root holds the prompt and whose other nodes hold generated token runs
+ * (DeFT reading notes, "decoding tree definition"). A query attends, with one
+ * softmax(Q K^T / sqrt(d)) V (FastTree review, section 3, core formula), to the
+ * concatenated KV of every node on its root-to-leaf path (DeFT notes, "tree
+ * attention definition"). Query j of a leaf with qpl queries is that leaf's
+ * token len - qpl + j and sees the leaf's tokens up to itself only; ancestors
+ * are fully visible. The result is exact: grouping and splitting change only
+ * the order of floating-point summation.
+ *
+ * How. tree_attn_plan() runs on the host once per tree: the greedy binary edge
+ * assignment of the FastTree review (section 3.2, Algorithm 1, with its
+ * padding and intermediate-result cost model) turns the tree into KV-guided
+ * context-query groups (DeFT notes, "KV-guided tree split"), long groups are
+ * cut into KV chunks (FastTree review, section 3.3), and the resulting tables
+ * are uploaded once. tree_attn_decode() then enqueues two HIP kernels on the
+ * caller's stream: one partial-attention launch over every (group, row block,
+ * KV chunk, kv-head) work item, which streams each chunk's paged KV from HBM
+ * once for all the queries of the group, and one log-sum-exp reduction that
+ * merges each query's partials along its path (DeFT notes, "tree-topology-aware
+ * global reduction").
+ *
+ * Conventions (all calls):
+ *  - Every call returns a ta_status; on failure tree_attn_last_error() gives a
+ *    thread-local message, valid until the next call on the same thread. No
+ *    C++ exception and no abort crosses this boundary.
+ *  - The caller owns every array it passes; the library copies what it needs
+ *    and keeps no caller pointer past the call (except device buffers handed
+ *    to tree_attn_decode, which must stay valid until the enqueued work ends).
+ *  - Node ids are 0..n_nodes-1 in any order. Leaves are ranked by ascending id.
+ *    Query index = leaf_rank * queries_per_leaf + j.
+ */
+#ifndef TREE_ATTN_H
+#define TREE_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ta_plan ta_plan; /* opaque; owned by the library */
+
+typedef enum {
+  TA_OK = 0,
+  TA_EINVAL = 1,      /* malformed tree, sizes or arguments */
+  TA_ENOMEM = 2,      /* host or device allocation failed */
+  TA_EHIP = 3,        /* a HIP runtime call failed */
+  TA_EUNSUPPORTED = 4 /* valid, but not supported (head_dim, dtype mix) */
+} ta_status;
+
+typedef enum { TA_F32 = 0, TA_BF16 = 1 } ta_dtype;
+
+/* Planner options. Any field left 0 takes its default. */
+typedef struct {
+  int32_t ts_q;    /* query tile of the padding cost (default 16) */
+  int32_t ts_c;    /* context tile of the padding cost and chunk alignment (default 64) */
+  int32_t gamma;   /* intermediate-result cost per query, in token units (default 32) */
+  int32_t rb;      /* maximum rows (query x q-head-in-group) per work item (default 256) */
+  int32_t waves;   /* target workgroups per CU for the split rule (default 4) */
+  int32_t floor_f; /* chunk length floor, in tokens per row (default 4) */
+  int32_t ncu;     /* compute units (default: the current device's count; 256 if host_only) */
+  int32_t no_split;/* 1 = never cut a group into KV chunks (default 0: split on) */
+  const int8_t* force_edges; /* NULL = greedy; else f[v] in {0,1} per node (root ignored) */
+  int32_t host_only;         /* 1 = build tables only, no HIP call (plan cannot decode) */
+  float scale;               /* softmax scale; 0 = 1/sqrt(head_dim) */
+  int32_t poison_workspace;  /* 1 = fill the workspace with NaN before every decode (testing) */
+} ta_plan_opts;
+
+/* Paged K/V pools on the device. Element strides; head_dim is contiguous.
+ * Token t of page p, kv-head h starts at base + p*stride_page + t*stride_token
+ * + h*stride_head. Default layout [n_pages, page_size, n_kvheads, head_dim]. */
+typedef struct {
+  const void* k;
+  const void* v;
+  ta_dtype dtype;
+  int32_t page_size;
+  int64_t n_pages;      /* pages in each pool; every page id of the plan must be < n_pages */
+  int64_t stride_page;
+  int64_t stride_token;
+  int64_t stride_head;
+} ta_paged_kv;
+
+/* Build a plan for one tree (host work; one upload of its tables).
+ *  parent[n_nodes]       : parent id, -1 for the single root. Must be acyclic.
+ *  node_kv_len[n_nodes]  : tokens per node, >= 1; a leaf has >= queries_per_leaf.
+ *  node_page_ptr[n+1], node_page_ids[]: CSR of each node's pages; node v has
+ *                          ceil(len/page_size) pages, token t in page t/page_size
+ *                          at slot t%page_size. Page ids in [0, 2^23).
+ *  page_size             : 1..256.
+ *  queries_per_leaf      : >= 1 (the leaf's last tokens are the queries).
+ *  n_qheads % n_kvheads == 0; q-head h reads kv-head h / (n_qheads/n_kvheads).
+ *  head_dim              : 64 or 128 (else TA_EUNSUPPORTED).
+ *  opts                  : NULL for defaults.
+ * On success *out_plan owns host tables, device tables and the fp32 partial
+ * workspace (size from tree_attn_plan_info). */
+ta_status tree_attn_plan(const int32_t* parent, int32_t n_nodes, const int32_t* node_kv_len,
+                         const int32_t* node_page_ptr, const int32_t* node_page_ids,
+                         int32_t page_size, int32_t queries_per_leaf, int32_t n_qheads,
+                         int32_t n_kvheads, int32_t head_dim, const ta_plan_opts* opts,
+                         ta_plan** out_plan);
+
+/* Enqueue one decode step on hip_stream (a hipStream_t; NULL = null stream).
+ *  q   : device [n_queries, n_qheads, head_dim], contiguous, q_dtype.
+ *  kv  : paged pools, dtype must equal q_dtype, page_size must equal the plan's.
+ *  out : device [n_queries, n_qheads, head_dim] fp32, contiguous.
+ * Asynchronous: returns after enqueueing. One plan serves one decode in
+ * flight at a time (its workspace is shared); the plan must outlive the work.
+ * TA_EINVAL for null pointers, dtype/page mismatches or page ids >= n_pages. */
+ta_status tree_attn_decode(const void* q, ta_dtype q_dtype, const ta_paged_kv* kv,
+                           const ta_plan* plan, float* out, void* hip_stream);
+
+/* Plan sizes. Any output pointer may be NULL. */
+ta_status tree_attn_plan_info(const ta_plan* plan, int32_t* n_queries, int64_t* workspace_bytes,
+                              int32_t* n_items);
+
+/* Export one plan table as int32 (table ids below). With dst == NULL only
+ * *len (element count) is written; otherwise dst must hold *len elements. */
+ta_status tree_attn_plan_export(const ta_plan* plan, int32_t table_id, int32_t* dst, int64_t* len);
+
+/* Timing of the last decodes (testing and benchmarking). After
+ * tree_attn_timing_enable(plan, capacity) every decode records HIP events
+ * around its two kernels on its stream, for up to `capacity` decodes
+ * (capacity 0 turns timing off). tree_attn_timing_read() waits for the
+ * recorded events and writes per-decode milliseconds of the partial-attention
+ * kernel and of the reduction kernel; *n gets the count and the record is
+ * cleared. */
+ta_status tree_attn_timing_enable(ta_plan* plan, int32_t capacity);
+ta_status tree_attn_timing_read(ta_plan* plan, float* partial_ms, float* reduce_ms, int32_t* n);
+
+/* Free a plan (synchronises the device first). NULL is a no-op. */
+void tree_attn_plan_destroy(ta_plan* plan);
+
+/* Thread-local message of the last failed call on this thread ("" if none). */
+const char* tree_attn_last_error(void);
+
+/* Table ids for tree_attn_plan_export (all int32, row-major). */
+enum {
+  TA_T_PARAMS = 0,        /* [24]: version, n_nodes, n_queries, qpl, n_qheads, n_kvheads,
+                             head_dim, page_size, ts_q, ts_c, gamma, rb, waves, floor_f, ncu,
+                             split, forced, chunk_align, n_groups, n_chunks, n_items, n_slots,
+                             c_glob, n_runs */
+  TA_T_EDGES = 1,         /* [n_nodes] f(parent -> v), 0 at the root */
+  TA_T_NQ = 2,            /* [n_nodes] queries left in v's virtual node */
+  TA_T_LCUM = 3,          /* [n_nodes] cumulative context length after merging */
+  TA_T_GROUPS = 4,        /* [n_groups x 8] node, top, kv_len, n_q, q_ptr, chunk_ptr, n_chunks,
+                             slot_base */
+  TA_T_GROUP_QS = 5,      /* [sum n_q] query ids per group, ascending */
+  TA_T_GROUP_VIS = 6,     /* [sum n_q] visible segment prefix per group query */
+  TA_T_CHUNKS = 7,        /* [n_chunks x 3] group, tok0, tok1 (segment positions) */
+  TA_T_ITEMS = 8,         /* [n_items x 4] group, row0, nrows, chunk; launch order */
+  TA_T_Q_SLOT_PTR = 9,    /* [n_queries + 1] */
+  TA_T_Q_SLOTS = 10,      /* partial slots of each query, root side first, chunks ascending */
+  TA_T_RUNS = 11,         /* [n_runs x 3] page id, first slot, tokens */
+  TA_T_CHUNK_RUN_PTR = 12,/* [n_chunks + 1] */
+  TA_T_BFS = 13,          /* [n_nodes] BFS order (children by ascending id) */
+  TA_T_COUNT = 14
+};
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREE_ATTN_H */

@@ -1,0 +1,181 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bar: max-abs error <= 3e-3 against the oracle, fp32 accumulation, on the
+exact bf16 / fp32 inputs the GPU sees. Every plan is built with the workspace
+poisoned with NaN before each decode, so a partial the kernels fail to write
+shows up as NaN in the output; unused KV slots hold V = 1e30 canaries, so an
+unmasked stray read shows up as a huge value.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import tree_attention as ta
+from tree_structured_shared_amd import Plan, TreeAttnError
+
+pytestmark = pytest.mark.gpu
+TOL = 3e-3
+
+
+def _dev(inst):
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    return inst.q.cuda(), inst.k_pool.cuda(), inst.v_pool.cuda()
+
+
+def _run(inst, dev=None, **plan_kw):
+    q, k, v = dev if dev is not None else _dev(inst)
+    plan_kw.setdefault("poison_workspace", True)
+    plan = Plan.for_instance(inst, **plan_kw)
+    out = plan.decode(q, k, v)
+    torch.cuda.synchronize()
+    res = out.cpu().numpy().astype(np.float64)
+    plan.close()
+    return res
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _check(got, ref, what):
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = np.nanmax(np.abs(got - ref))
+    _log(f"{what}: max-abs err {err:.3e}")
+    assert err <= TOL, f"{what}: max-abs err {err:.3e}"
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4])
+def test_workload_full(k):
+    _log(f"config {k}")
+    inst = synth.make_config(k)
+    ref = ta.decode_instance(inst)
+    got = _run(inst)
+    _check(got, ref, f"config {k}")
+
+
+def test_workload5_full():
+    _log("config 5")
+    inst = synth.make_config(5)
+    dev = _dev(inst)
+    got = _run(inst, dev)
+    ref = ta.decode_instance(inst)
+    _check(got, ref, "config 5")
+
+
+@pytest.mark.parametrize("k", [2, 5])
+def test_plan_invariance(k):
+    """Grouping and splitting change only summation order: forced all-0,
+    all-1 and random edges, split off and other chunk sizes agree with the
+    oracle too."""
+    inst = synth.make_config(k)
+    dev = _dev(inst)
+    n = inst.n_nodes
+    leaves = None if k == 2 else list(range(0, inst.n_leaves, 7))
+    ref = ta.decode_instance(inst, leaves=leaves)
+    rows = ~np.isnan(ref[:, 0, 0])
+    rng = np.random.default_rng(k)
+    variants = [dict(force_edges=[0] * n), dict(force_edges=[1] * n),
+                dict(force_edges=rng.integers(0, 2, n).tolist()), dict(split=False),
+                dict(ncu=1024, ts_c=16), dict(rb=32, floor_f=1), dict(waves=1, ncu=64)]
+    for kw in variants:
+        got = _run(inst, dev, **kw)
+        _check(got[rows], ref[rows], f"config {k} {kw if 'force_edges' not in kw else 'forced'}")
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_trees(seed):
+    inst = synth.random_small_tree(seed, max_nodes=30, max_len=300)
+    _log(f"random tree {seed}: n={inst.n_nodes} qpl={inst.qpl} heads={inst.n_qheads}/{inst.n_kvheads} "
+         f"d={inst.head_dim} ps={inst.page_size} {inst.dtype}")
+    ref = ta.decode_instance(inst)
+    kw = {}
+    if seed % 3 == 0:
+        kw = dict(ncu=512, ts_c=16)      # many small chunks, ragged tails
+    _check(_run(inst, **kw), ref, f"random tree {seed}")
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 64), (torch.bfloat16, 128),
+                                     (torch.float32, 64), (torch.float32, 128)])
+@pytest.mark.parametrize("rows_case", ["gemv", "mid", "wide"])
+def test_row_paths(dtype, d, rows_case):
+    """Each row path of the partial kernel: GEMV-sized (1-4 rows), one MFMA
+    pass (<= 64 rows) and several row passes (> 128 rows)."""
+    hq, h, n_leaf, qpl = {"gemv": (4, 1, 1, 1), "mid": (8, 2, 5, 3), "wide": (16, 1, 12, 2)}[rows_case]
+    par = [-1] + [0] * n_leaf
+    lens = [517] + [40 + 7 * i for i in range(n_leaf)]
+    inst = synth.make_tree(par, lens, page_size=16, qpl=qpl, n_qheads=hq, n_kvheads=h, head_dim=d,
+                           dtype=dtype, seed=3)
+    synth.fill_tensors(inst, seed=21)
+    ref = ta.decode_instance(inst)
+    _check(_run(inst), ref, f"rows {rows_case} {dtype} d{d}")
+    _check(_run(inst, rb=256, split=False), ref, f"rows {rows_case} {dtype} d{d} rb256 nosplit")
+
+
+def test_edge_cases():
+    cases = [
+        ([-1], [1], 1),                 # one node, one token
+        ([-1], [5], 5),                 # first query sees one token only
+        ([-1, 0], [1, 1], 1),           # one-token nodes
+        ([-1, 0, 0, 1], [33, 17, 1, 64], 1),
+    ]
+    for ps in (1, 16, 256):
+        for par, lens, qpl in cases:
+            for dtype in (torch.bfloat16, torch.float32):
+                inst = synth.make_tree(par, lens, page_size=ps, qpl=qpl, n_qheads=8, n_kvheads=2,
+                                       head_dim=128, dtype=dtype, seed=1)
+                synth.fill_tensors(inst, seed=2)
+                ref = ta.decode_instance(inst)
+                _check(_run(inst), ref, f"edge {par} {lens} qpl{qpl} ps{ps} {dtype}")
+
+
+def test_max_rows_per_item():
+    """A group with many rows (root of 300 queries x GQA 8 = 2400 rows) spans
+    several row blocks."""
+    n_leaf = 300
+    inst = synth.make_tree([-1] + [0] * n_leaf, [700] + [3] * n_leaf, page_size=16, qpl=1,
+                           n_qheads=32, n_kvheads=4, head_dim=128, dtype=torch.bfloat16, seed=5)
+    synth.fill_tensors(inst, seed=6)
+    ref = ta.decode_instance(inst, leaves=list(range(0, n_leaf, 13)))
+    got = _run(inst)
+    rows = ~np.isnan(ref[:, 0, 0])
+    _check(got[rows], ref[rows], "2400-row root")
+
+
+def test_repeat_decodes_identical():
+    inst = synth.make_config(3)
+    q, k, v = _dev(inst)
+    plan = Plan.for_instance(inst)
+    a = plan.decode(q, k, v).clone()
+    b = plan.decode(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    plan.close()
+
+
+def test_decode_argument_errors():
+    inst = synth.make_config(1)
+    q, k, v = _dev(inst)
+    plan = Plan.for_instance(inst)
+    with pytest.raises(TreeAttnError):
+        plan.decode(q.to(torch.bfloat16), k, v)           # dtype mismatch
+    with pytest.raises(TreeAttnError):
+        plan.decode(q, k[:2], v[:2])                      # pool smaller than the plan's pages
+    with pytest.raises(TreeAttnError):
+        plan.decode(q[:2], k, v)                          # wrong query count
+    plan.close()
+
+
+def test_timing_records():
+    inst = synth.make_config(2)
+    q, k, v = _dev(inst)
+    plan = Plan.for_instance(inst)
+    plan.timing_enable(4)
+    for _ in range(3):
+        plan.decode(q, k, v)
+    pm, rm = plan.timing_read(4)
+    assert len(pm) == 3 and (pm > 0).all() and (rm > 0).all()
+    plan.close()

@@ -1,0 +1,163 @@
+"""Tree-structured decode attention for MI355X (gfx950).
+
+A thin binding over the C ABI of ``libtree_attn.so`` (include/tree_attn.h):
+argument checks and marshalling only. Planning runs in the library's C++ host
+code and every step of the decode runs in its HIP kernels; PyTorch supplies
+device memory and the stream.
+
+    plan = Plan(parent, node_kv_len, node_page_ptr, node_page_ids, page_size,
+                queries_per_leaf, n_qheads, n_kvheads, head_dim)
+    out = plan.decode(q, k_pool, v_pool)      # fp32 [n_queries, n_qheads, head_dim]
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+
+from ._capi import (TA_BF16, TA_F32, TABLE_COLS, TABLE_IDS, PagedKV, PlanOpts, TreeAttnError,
+                    check, lib)
+
+__all__ = ["Plan", "TreeAttnError", "TABLE_IDS"]
+
+
+def _i32(a):
+    arr = np.ascontiguousarray(np.asarray(a), dtype=np.int32)
+    return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+class Plan:
+    """A decode plan for one tree (owns device tables and the partial workspace)."""
+
+    def __init__(self, parent, node_kv_len, node_page_ptr, node_page_ids, page_size,
+                 queries_per_leaf, n_qheads, n_kvheads, head_dim, *, force_edges=None,
+                 host_only=False, scale=0.0, poison_workspace=False, ts_q=0, ts_c=0, gamma=0,
+                 rb=0, waves=0, floor_f=0, ncu=0, split=True):
+        L = lib()
+        self._handle = ctypes.c_void_p()
+        par, par_p = _i32(parent)
+        lens, lens_p = _i32(node_kv_len)
+        ptr, ptr_p = _i32(node_page_ptr)
+        ids, ids_p = _i32(node_page_ids)
+        if len(lens) != len(par) or len(ptr) != len(par) + 1:
+            raise TreeAttnError(1, "parent / node_kv_len / node_page_ptr sizes disagree")
+        if len(ids) < (int(ptr[-1]) if len(ptr) else 0):
+            raise TreeAttnError(1, "node_page_ids shorter than node_page_ptr[-1]")
+        opts = PlanOpts(ts_q=ts_q, ts_c=ts_c, gamma=gamma, rb=rb, waves=waves, floor_f=floor_f,
+                        ncu=ncu, no_split=0 if split else 1, host_only=1 if host_only else 0,
+                        scale=float(scale), poison_workspace=1 if poison_workspace else 0)
+        self._force = None
+        if force_edges is not None:
+            fe = np.ascontiguousarray(np.asarray(force_edges), dtype=np.int8)
+            if len(fe) != len(par):
+                raise TreeAttnError(1, "force_edges must have one entry per node")
+            self._force = fe
+            opts.force_edges = fe.ctypes.data_as(ctypes.POINTER(ctypes.c_int8))
+        check(L.tree_attn_plan(par_p, len(par), lens_p, ptr_p, ids_p, int(page_size),
+                               int(queries_per_leaf), int(n_qheads), int(n_kvheads), int(head_dim),
+                               ctypes.byref(opts), ctypes.byref(self._handle)))
+        self.page_size = int(page_size)
+        self.n_qheads = int(n_qheads)
+        self.n_kvheads = int(n_kvheads)
+        self.head_dim = int(head_dim)
+        self.host_only = bool(host_only)
+        nq = ctypes.c_int32()
+        ws = ctypes.c_int64()
+        ni = ctypes.c_int32()
+        check(L.tree_attn_plan_info(self._handle, ctypes.byref(nq), ctypes.byref(ws), ctypes.byref(ni)))
+        self.n_queries, self.workspace_bytes, self.n_items = nq.value, ws.value, ni.value
+
+    @classmethod
+    def for_instance(cls, inst, **kw):
+        return cls(inst.parent, inst.node_len, inst.node_page_ptr, inst.node_page_ids,
+                   inst.page_size, inst.qpl, inst.n_qheads, inst.n_kvheads, inst.head_dim, **kw)
+
+    # -- tables ---------------------------------------------------------------
+    def export(self, name):
+        tid = TABLE_IDS[name] if isinstance(name, str) else int(name)
+        n = ctypes.c_int64()
+        check(lib().tree_attn_plan_export(self._handle, tid, None, ctypes.byref(n)))
+        out = np.zeros(n.value, dtype=np.int32)
+        check(lib().tree_attn_plan_export(self._handle, tid,
+                                          out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                          ctypes.byref(n)))
+        cols = TABLE_COLS.get(name if isinstance(name, str) else "")
+        return out.reshape(-1, cols) if cols else out
+
+    def tables(self):
+        return {k: self.export(k) for k in TABLE_IDS}
+
+    # -- decode ---------------------------------------------------------------
+    def decode(self, q, k_pool, v_pool, out=None, stream=None):
+        """Enqueue one decode step; returns ``out`` (fp32 [n_queries, n_qheads, head_dim])."""
+        call, out = self._prepare(q, k_pool, v_pool, out, stream)
+        call()
+        return out
+
+    def launcher(self, q, k_pool, v_pool, out, stream=None):
+        """Check the tensors once and return a zero-argument callable that
+        enqueues tree_attn_decode with the prepared arguments (for loops that
+        decode the same buffers repeatedly)."""
+        return self._prepare(q, k_pool, v_pool, out, stream)[0]
+
+    def _prepare(self, q, k_pool, v_pool, out, stream):
+        import torch
+        if self.host_only:
+            raise TreeAttnError(1, "plan was built host_only")
+        dt = {torch.float32: TA_F32, torch.bfloat16: TA_BF16}.get(q.dtype)
+        if dt is None:
+            raise TreeAttnError(4, f"unsupported dtype {q.dtype}")
+        for name, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool)):
+            if not t.is_cuda:
+                raise TreeAttnError(1, f"{name} must be a device tensor")
+            if t.dtype != q.dtype:
+                raise TreeAttnError(4, f"{name} dtype {t.dtype} differs from q's {q.dtype}")
+        if tuple(q.shape) != (self.n_queries, self.n_qheads, self.head_dim) or not q.is_contiguous():
+            raise TreeAttnError(1, f"q must be contiguous [{self.n_queries}, {self.n_qheads}, {self.head_dim}]")
+        if k_pool.dim() != 4 or tuple(k_pool.shape[1:]) != (self.page_size, self.n_kvheads, self.head_dim):
+            raise TreeAttnError(1, "k_pool must be [n_pages, page_size, n_kvheads, head_dim]")
+        if k_pool.shape != v_pool.shape or k_pool.stride() != v_pool.stride():
+            raise TreeAttnError(1, "k_pool and v_pool must have the same shape and strides")
+        if k_pool.stride(3) != 1:
+            raise TreeAttnError(1, "head_dim must be contiguous in the pools")
+        if out is None:
+            out = torch.empty((self.n_queries, self.n_qheads, self.head_dim), dtype=torch.float32,
+                              device=q.device)
+        elif (out.dtype != torch.float32 or not out.is_contiguous()
+              or tuple(out.shape) != (self.n_queries, self.n_qheads, self.head_dim)):
+            raise TreeAttnError(1, "out must be contiguous fp32 [n_queries, n_qheads, head_dim]")
+        kv = PagedKV(k=k_pool.data_ptr(), v=v_pool.data_ptr(), dtype=dt, page_size=self.page_size,
+                     n_pages=k_pool.shape[0], stride_page=k_pool.stride(0),
+                     stride_token=k_pool.stride(1), stride_head=k_pool.stride(2))
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device).cuda_stream
+        fn = lib().tree_attn_decode
+        args = (ctypes.c_void_p(q.data_ptr()), dt, ctypes.byref(kv), self._handle,
+                ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream))
+        keep = (kv, q, k_pool, v_pool, out)
+
+        def call(_fn=fn, _args=args, _keep=keep):
+            check(_fn(*_args))
+        return call, out
+
+    # -- timing ---------------------------------------------------------------
+    def timing_enable(self, capacity):
+        check(lib().tree_attn_timing_enable(self._handle, int(capacity)))
+
+    def timing_read(self, capacity):
+        pm = (ctypes.c_float * max(1, capacity))()
+        rm = (ctypes.c_float * max(1, capacity))()
+        n = ctypes.c_int32()
+        check(lib().tree_attn_timing_read(self._handle, pm, rm, ctypes.byref(n)))
+        return np.array(pm[:n.value]), np.array(rm[:n.value])
+
+    def close(self):
+        if getattr(self, "_handle", None) and self._handle.value:
+            lib().tree_attn_plan_destroy(self._handle)
+            self._handle = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,390 @@
+// C ABI of the tree-attention library: plan lifetime, table export, decode
+// launches and kernel timing. Declared in include/tree_attn.h.
+#include "tree_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "planner.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+ta_status set_err(ta_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+ta_status hip_err(hipError_t e, const char* where) {
+  return set_err(TA_EHIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+}  // namespace
+
+struct ta_plan {
+  ta::PlanTables T;
+  int32_t host_only = 0, head_dim = 0, n_qheads = 0, n_kvheads = 0, g = 1, page_size = 0, qpl = 0;
+  float scale = 0.0f;
+  int32_t poison = 0;
+  int device = -1;
+  void* d_tables = nullptr;  // one allocation for every device table
+  ta::WorkItem* d_items = nullptr;
+  int32_t *d_group_qs = nullptr, *d_group_vis = nullptr, *d_seg_tok = nullptr;
+  int32_t *d_q_slot_ptr = nullptr, *d_q_slots = nullptr;
+  void* d_ws = nullptr;  // workspace: o_part | m_part | l_part
+  float *d_o_part = nullptr, *d_m_part = nullptr, *d_l_part = nullptr;
+  int64_t ws_bytes = 0;
+  std::vector<hipEvent_t> ev;  // 3 per timed decode
+  int32_t timing_cap = 0, timing_n = 0;
+};
+
+namespace {
+
+const std::vector<int32_t>* table_ptr(const ta_plan* p, int32_t id) {
+  const ta::PlanTables& T = p->T;
+  switch (id) {
+    case TA_T_PARAMS: return &T.params;
+    case TA_T_EDGES: return &T.edges;
+    case TA_T_NQ: return &T.nq;
+    case TA_T_LCUM: return &T.lcum;
+    case TA_T_GROUPS: return &T.groups;
+    case TA_T_GROUP_QS: return &T.group_qs;
+    case TA_T_GROUP_VIS: return &T.group_vis;
+    case TA_T_CHUNKS: return &T.chunks;
+    case TA_T_ITEMS: return &T.items;
+    case TA_T_Q_SLOT_PTR: return &T.q_slot_ptr;
+    case TA_T_Q_SLOTS: return &T.q_slots;
+    case TA_T_RUNS: return &T.runs;
+    case TA_T_CHUNK_RUN_PTR: return &T.chunk_run_ptr;
+    case TA_T_BFS: return &T.bfs;
+    default: return nullptr;
+  }
+}
+
+void free_device(ta_plan* p) {
+  if (p->host_only) return;
+  for (hipEvent_t e : p->ev) (void)hipEventDestroy(e);
+  p->ev.clear();
+  if (p->d_tables) (void)hipFree(p->d_tables);
+  if (p->d_ws) (void)hipFree(p->d_ws);
+  p->d_tables = p->d_ws = nullptr;
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+ta_status upload(ta_plan* p) {
+  const ta::PlanTables& T = p->T;
+  // work items in launch order
+  std::vector<ta::WorkItem> items(T.n_items);
+  for (int32_t x = 0; x < T.n_items; ++x) {
+    const int32_t gi = T.items[4 * x], r0 = T.items[4 * x + 1], nr = T.items[4 * x + 2],
+                  ci = T.items[4 * x + 3];
+    const int32_t* G = &T.groups[8 * gi];
+    ta::WorkItem w{};
+    w.q_ptr = G[4];
+    w.row0 = r0;
+    w.nrows = nr;
+    w.tok0 = T.chunks[3 * ci + 1];
+    w.tok1 = T.chunks[3 * ci + 2];
+    w.seg_base = T.group_seg_base[gi];
+    w.slot0 = G[7] + (ci - G[5]) * G[3];
+    items[x] = w;
+  }
+  const size_t sz_items = items.size() * sizeof(ta::WorkItem);
+  const size_t sz_qs = T.group_qs.size() * 4, sz_vis = T.group_vis.size() * 4,
+               sz_seg = T.seg_tok.size() * 4, sz_qsp = T.q_slot_ptr.size() * 4,
+               sz_qsl = T.q_slots.size() * 4;
+  size_t off[6], total = 0;
+  const size_t sizes[6] = {sz_items, sz_qs, sz_vis, sz_seg, sz_qsp, sz_qsl};
+  for (int x = 0; x < 6; ++x) {
+    off[x] = total;
+    total += align256(sizes[x] ? sizes[x] : 1);
+  }
+  hipError_t e = hipMalloc(&p->d_tables, total);
+  if (e != hipSuccess) {
+    p->d_tables = nullptr;
+    return set_err(TA_ENOMEM, std::string("tree_attn_plan: hipMalloc(tables): ") + hipGetErrorString(e));
+  }
+  std::vector<uint8_t> host(total, 0);
+  const void* src[6] = {items.data(), T.group_qs.data(), T.group_vis.data(), T.seg_tok.data(),
+                        T.q_slot_ptr.data(), T.q_slots.data()};
+  for (int x = 0; x < 6; ++x)
+    if (sizes[x]) std::memcpy(host.data() + off[x], src[x], sizes[x]);
+  e = hipMemcpy(p->d_tables, host.data(), total, hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_err(e, "tree_attn_plan: hipMemcpy(tables)");
+  uint8_t* base = static_cast<uint8_t*>(p->d_tables);
+  p->d_items = reinterpret_cast<ta::WorkItem*>(base + off[0]);
+  p->d_group_qs = reinterpret_cast<int32_t*>(base + off[1]);
+  p->d_group_vis = reinterpret_cast<int32_t*>(base + off[2]);
+  p->d_seg_tok = reinterpret_cast<int32_t*>(base + off[3]);
+  p->d_q_slot_ptr = reinterpret_cast<int32_t*>(base + off[4]);
+  p->d_q_slots = reinterpret_cast<int32_t*>(base + off[5]);
+
+  const size_t n_pairs = size_t(T.n_slots) * p->n_qheads;
+  const size_t sz_o = align256(n_pairs * p->head_dim * 4), sz_m = align256(n_pairs * 4);
+  p->ws_bytes = int64_t(sz_o + 2 * sz_m);
+  e = hipMalloc(&p->d_ws, size_t(p->ws_bytes));
+  if (e != hipSuccess) {
+    p->d_ws = nullptr;
+    return set_err(TA_ENOMEM, std::string("tree_attn_plan: hipMalloc(workspace): ") + hipGetErrorString(e));
+  }
+  uint8_t* wb = static_cast<uint8_t*>(p->d_ws);
+  p->d_o_part = reinterpret_cast<float*>(wb);
+  p->d_m_part = reinterpret_cast<float*>(wb + sz_o);
+  p->d_l_part = reinterpret_cast<float*>(wb + sz_o + sz_m);
+  return TA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ta_status tree_attn_plan(const int32_t* parent, int32_t n_nodes, const int32_t* node_kv_len,
+                         const int32_t* node_page_ptr, const int32_t* node_page_ids,
+                         int32_t page_size, int32_t queries_per_leaf, int32_t n_qheads,
+                         int32_t n_kvheads, int32_t head_dim, const ta_plan_opts* opts,
+                         ta_plan** out_plan) {
+  g_err.clear();
+  if (!out_plan) return set_err(TA_EINVAL, "tree_attn_plan: out_plan is NULL");
+  *out_plan = nullptr;
+  ta_plan* p = nullptr;
+  try {
+    ta::PlanParams pp;
+    int32_t host_only = 0, poison = 0;
+    float scale = 0.0f;
+    if (opts) {
+      if (opts->ts_q) pp.ts_q = opts->ts_q;
+      if (opts->ts_c) pp.ts_c = opts->ts_c;
+      if (opts->gamma) pp.gamma = opts->gamma;
+      if (opts->rb) pp.rb = opts->rb;
+      if (opts->waves) pp.waves = opts->waves;
+      if (opts->floor_f) pp.floor_f = opts->floor_f;
+      pp.split = opts->no_split ? 0 : 1;
+      pp.force_edges = opts->force_edges;
+      host_only = opts->host_only ? 1 : 0;
+      poison = opts->poison_workspace ? 1 : 0;
+      scale = opts->scale;
+      if (opts->ncu) pp.ncu = opts->ncu;
+    }
+    int device = -1;
+    if (!host_only) {
+      hipError_t e = hipGetDevice(&device);
+      if (e != hipSuccess) return hip_err(e, "tree_attn_plan: hipGetDevice");
+      if (!(opts && opts->ncu)) {
+        int ncu = 0;
+        e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, device);
+        if (e != hipSuccess) return hip_err(e, "tree_attn_plan: hipDeviceGetAttribute");
+        pp.ncu = ncu;
+      }
+    }
+    if (!(scale >= 0.0f) || std::isinf(scale)) return set_err(TA_EINVAL, "tree_attn_plan: bad scale");
+    p = new ta_plan;
+    std::string err;
+    const int rc = ta::build_plan(parent, n_nodes, node_kv_len, node_page_ptr, node_page_ids,
+                                  page_size, queries_per_leaf, n_qheads, n_kvheads, head_dim, pp,
+                                  &p->T, &err);
+    if (rc != 0) {
+      delete p;
+      return set_err(ta_status(rc), err);
+    }
+    p->host_only = host_only;
+    p->head_dim = head_dim;
+    p->n_qheads = n_qheads;
+    p->n_kvheads = n_kvheads;
+    p->g = n_qheads / n_kvheads;
+    p->page_size = page_size;
+    p->qpl = queries_per_leaf;
+    p->scale = scale > 0.0f ? scale : 1.0f / std::sqrt(float(head_dim));
+    p->poison = poison;
+    p->device = device;
+    if (!host_only) {
+      const ta_status s = upload(p);
+      if (s != TA_OK) {
+        free_device(p);
+        delete p;
+        return s;
+      }
+    }
+    *out_plan = p;
+    return TA_OK;
+  } catch (const std::bad_alloc&) {
+    delete p;
+    return set_err(TA_ENOMEM, "tree_attn_plan: host allocation failed");
+  } catch (...) {
+    delete p;
+    return set_err(TA_EINVAL, "tree_attn_plan: unexpected failure");
+  }
+}
+
+ta_status tree_attn_decode(const void* q, ta_dtype q_dtype, const ta_paged_kv* kv,
+                           const ta_plan* plan, float* out, void* hip_stream) {
+  g_err.clear();
+  if (!plan) return set_err(TA_EINVAL, "tree_attn_decode: plan is NULL");
+  if (plan->host_only) return set_err(TA_EINVAL, "tree_attn_decode: plan was built host_only");
+  if (!q || !kv || !out || !kv->k || !kv->v)
+    return set_err(TA_EINVAL, "tree_attn_decode: NULL pointer argument");
+  if (q_dtype != TA_F32 && q_dtype != TA_BF16)
+    return set_err(TA_EUNSUPPORTED, "tree_attn_decode: dtype must be TA_F32 or TA_BF16");
+  if (kv->dtype != q_dtype)
+    return set_err(TA_EUNSUPPORTED, "tree_attn_decode: Q and KV dtypes differ");
+  if (kv->page_size != plan->page_size)
+    return set_err(TA_EINVAL, "tree_attn_decode: page_size differs from the plan's");
+  if (kv->n_pages <= int64_t(plan->T.max_page_id))
+    return set_err(TA_EINVAL, "tree_attn_decode: the plan references pages beyond kv->n_pages");
+  const int64_t vec = (q_dtype == TA_BF16) ? 8 : 4;  // elements per 16 bytes
+  if (kv->stride_page <= 0 || kv->stride_token <= 0 || kv->stride_head <= 0 ||
+      kv->stride_page % vec || kv->stride_token % vec || kv->stride_head % vec)
+    return set_err(TA_EINVAL, "tree_attn_decode: strides must be positive multiples of 16 bytes");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(kv->k) |
+       reinterpret_cast<uintptr_t>(kv->v) | reinterpret_cast<uintptr_t>(out)) & 15)
+    return set_err(TA_EINVAL, "tree_attn_decode: pointers must be 16-byte aligned");
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_err(e, "tree_attn_decode: hipGetDevice");
+  if (dev != plan->device) return set_err(TA_EINVAL, "tree_attn_decode: current device differs from the plan's");
+
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  ta_plan* mp = const_cast<ta_plan*>(plan);
+  const bool timed = mp->timing_cap > 0 && mp->timing_n < mp->timing_cap;
+  if (mp->poison) {
+    e = ta::launch_fill(mp->d_o_part, mp->ws_bytes / 4, std::nanf(""), s);
+    if (e != hipSuccess) return hip_err(e, "tree_attn_decode: poison fill");
+  }
+  if (timed && (e = hipEventRecord(mp->ev[3 * mp->timing_n], s)) != hipSuccess)
+    return hip_err(e, "tree_attn_decode: hipEventRecord");
+
+  ta::PartialArgs a{};
+  a.items = plan->d_items;
+  a.group_qs = plan->d_group_qs;
+  a.group_vis = plan->d_group_vis;
+  a.seg_tok = plan->d_seg_tok;
+  a.q = q;
+  a.k = kv->k;
+  a.v = kv->v;
+  a.stride_page = kv->stride_page;
+  a.stride_token = kv->stride_token;
+  a.stride_head = kv->stride_head;
+  a.o_part = plan->d_o_part;
+  a.m_part = plan->d_m_part;
+  a.l_part = plan->d_l_part;
+  a.n_qheads = plan->n_qheads;
+  a.n_kvheads = plan->n_kvheads;
+  a.g = plan->g;
+  a.scale_log2 = plan->scale * 1.4426950408889634f;
+  e = ta::launch_partial(a, plan->T.n_items * plan->n_kvheads, q_dtype == TA_BF16 ? 1 : 0,
+                         plan->head_dim, s);
+  if (e != hipSuccess) return hip_err(e, "tree_attn_decode: partial-attention launch");
+  if (timed && (e = hipEventRecord(mp->ev[3 * mp->timing_n + 1], s)) != hipSuccess)
+    return hip_err(e, "tree_attn_decode: hipEventRecord");
+
+  ta::ReduceArgs r{};
+  r.q_slot_ptr = plan->d_q_slot_ptr;
+  r.q_slots = plan->d_q_slots;
+  r.o_part = plan->d_o_part;
+  r.m_part = plan->d_m_part;
+  r.l_part = plan->d_l_part;
+  r.out = out;
+  r.n_queries = plan->T.n_queries;
+  r.n_qheads = plan->n_qheads;
+  e = ta::launch_reduce(r, plan->head_dim, s);
+  if (e != hipSuccess) return hip_err(e, "tree_attn_decode: reduction launch");
+  if (timed) {
+    if ((e = hipEventRecord(mp->ev[3 * mp->timing_n + 2], s)) != hipSuccess)
+      return hip_err(e, "tree_attn_decode: hipEventRecord");
+    ++mp->timing_n;
+  }
+  return TA_OK;
+}
+
+ta_status tree_attn_plan_info(const ta_plan* plan, int32_t* n_queries, int64_t* workspace_bytes,
+                              int32_t* n_items) {
+  g_err.clear();
+  if (!plan) return set_err(TA_EINVAL, "tree_attn_plan_info: plan is NULL");
+  if (n_queries) *n_queries = plan->T.n_queries;
+  if (workspace_bytes) {
+    if (plan->host_only) {
+      const int64_t pairs = int64_t(plan->T.n_slots) * plan->n_qheads;
+      *workspace_bytes = int64_t(align256(size_t(pairs) * plan->head_dim * 4)) + 2 * int64_t(align256(size_t(pairs) * 4));
+    } else {
+      *workspace_bytes = plan->ws_bytes;
+    }
+  }
+  if (n_items) *n_items = plan->T.n_items;
+  return TA_OK;
+}
+
+ta_status tree_attn_plan_export(const ta_plan* plan, int32_t table_id, int32_t* dst, int64_t* len) {
+  g_err.clear();
+  if (!plan || !len) return set_err(TA_EINVAL, "tree_attn_plan_export: NULL plan or len");
+  const std::vector<int32_t>* t = table_ptr(plan, table_id);
+  if (!t) return set_err(TA_EINVAL, "tree_attn_plan_export: unknown table id");
+  if (dst) {
+    if (*len < int64_t(t->size())) return set_err(TA_EINVAL, "tree_attn_plan_export: dst too small");
+    if (!t->empty()) std::memcpy(dst, t->data(), t->size() * sizeof(int32_t));
+  }
+  *len = int64_t(t->size());
+  return TA_OK;
+}
+
+ta_status tree_attn_timing_enable(ta_plan* plan, int32_t capacity) {
+  g_err.clear();
+  if (!plan) return set_err(TA_EINVAL, "tree_attn_timing_enable: plan is NULL");
+  if (plan->host_only) return set_err(TA_EINVAL, "tree_attn_timing_enable: host_only plan");
+  if (capacity < 0) return set_err(TA_EINVAL, "tree_attn_timing_enable: negative capacity");
+  for (hipEvent_t e : plan->ev) (void)hipEventDestroy(e);
+  plan->ev.clear();
+  plan->timing_cap = 0;
+  plan->timing_n = 0;
+  try {
+    plan->ev.resize(size_t(capacity) * 3);
+  } catch (const std::bad_alloc&) {
+    return set_err(TA_ENOMEM, "tree_attn_timing_enable: host allocation failed");
+  }
+  for (size_t x = 0; x < plan->ev.size(); ++x) {
+    hipError_t e = hipEventCreate(&plan->ev[x]);
+    if (e != hipSuccess) {
+      plan->ev.resize(x);
+      return hip_err(e, "tree_attn_timing_enable: hipEventCreate");
+    }
+  }
+  plan->timing_cap = capacity;
+  return TA_OK;
+}
+
+ta_status tree_attn_timing_read(ta_plan* plan, float* partial_ms, float* reduce_ms, int32_t* n) {
+  g_err.clear();
+  if (!plan || !n) return set_err(TA_EINVAL, "tree_attn_timing_read: NULL argument");
+  const int32_t cnt = plan->timing_n;
+  for (int32_t x = 0; x < cnt; ++x) {
+    hipError_t e = hipEventSynchronize(plan->ev[3 * x + 2]);
+    if (e != hipSuccess) return hip_err(e, "tree_attn_timing_read: hipEventSynchronize");
+    float t0 = 0.0f, t1 = 0.0f;
+    if ((e = hipEventElapsedTime(&t0, plan->ev[3 * x], plan->ev[3 * x + 1])) != hipSuccess)
+      return hip_err(e, "tree_attn_timing_read: hipEventElapsedTime");
+    if ((e = hipEventElapsedTime(&t1, plan->ev[3 * x + 1], plan->ev[3 * x + 2])) != hipSuccess)
+      return hip_err(e, "tree_attn_timing_read: hipEventElapsedTime");
+    if (partial_ms) partial_ms[x] = t0;
+    if (reduce_ms) reduce_ms[x] = t1;
+  }
+  *n = cnt;
+  plan->timing_n = 0;
+  return TA_OK;
+}
+
+void tree_attn_plan_destroy(ta_plan* plan) {
+  if (!plan) return;
+  if (!plan->host_only) (void)hipDeviceSynchronize();
+  free_device(plan);
+  delete plan;
+}
+
+const char* tree_attn_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,55 @@
+// Device-side work description and kernel launchers (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace ta {
+
+// One work item of the partial-attention launch (built from the plan's
+// ITEMS/GROUPS/CHUNKS tables at plan time). Rows r in [row0, row0 + nrows) of
+// the group map to group query r / g and q-head-in-group r % g.
+struct WorkItem {
+  int32_t q_ptr;     // offset of the group's queries in group_qs / group_vis
+  int32_t row0;      // first row of the block
+  int32_t nrows;     // rows in the block (<= rb)
+  int32_t tok0;      // chunk start (segment position)
+  int32_t tok1;      // chunk end (exclusive)
+  int32_t seg_base;  // offset of the group's segment in seg_tok
+  int32_t slot0;     // slot of the chunk's first group query: slot_base + chunk * n_q
+  int32_t pad;
+};
+
+struct PartialArgs {
+  const WorkItem* items;
+  const int32_t* group_qs;
+  const int32_t* group_vis;
+  const int32_t* seg_tok;  // (page << 8) | slot per segment token
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t stride_page, stride_token, stride_head;  // elements
+  float* o_part;   // [n_slots, n_qheads, D] unnormalised
+  float* m_part;   // [n_slots, n_qheads] running max, base-2 scaled units
+  float* l_part;   // [n_slots, n_qheads] sum of exp2(s - m)
+  int32_t n_qheads, n_kvheads, g;
+  float scale_log2;  // softmax scale * log2(e)
+};
+
+struct ReduceArgs {
+  const int32_t* q_slot_ptr;
+  const int32_t* q_slots;
+  const float* o_part;
+  const float* m_part;
+  const float* l_part;
+  float* out;  // [n_q, n_qheads, D]
+  int32_t n_queries, n_qheads;
+};
+
+// dtype: 0 = fp32, 1 = bf16 (Q, K and V share it).
+hipError_t launch_partial(const PartialArgs& a, int32_t n_work, int dtype, int head_dim,
+                          hipStream_t s);
+hipError_t launch_reduce(const ReduceArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_fill(float* p, int64_t n, float value, hipStream_t s);
+
+}  // namespace ta
