@@ -60,7 +60,7 @@ typedef struct {
   int32_t ts_c;    /* context tile of the padding cost and chunk alignment (default 64) */
   int32_t gamma;   /* intermediate-result cost per query, in token units (default 32) */
   int32_t rb;      /* maximum rows (query x q-head-in-group) per work item (default 256) */
-  int32_t waves;   /* target workgroups per CU for the split rule (default 4) */
+  int32_t waves;   /* target busy waves per CU for the split rule (default 8) */
   int32_t floor_f; /* chunk length floor, in tokens per row (default 4) */
   int32_t ncu;     /* compute units (default: the current device's count; 256 if host_only) */
   int32_t no_split;/* 1 = never cut a group into KV chunks (default 0: split on) */
@@ -68,6 +68,8 @@ typedef struct {
   int32_t host_only;         /* 1 = build tables only, no HIP call (plan cannot decode) */
   float scale;               /* softmax scale; 0 = 1/sqrt(head_dim) */
   int32_t poison_workspace;  /* 1 = fill the workspace with NaN before every decode (testing) */
+  int32_t stream_rows;       /* groups with at most this many rows (query x q-head-in-group)
+                                run as single-wave items (default 16; -1 = none) */
 } ta_plan_opts;
 
 /* Paged K/V pools on the device. Element strides; head_dim is contiguous.
@@ -139,10 +141,10 @@ const char* tree_attn_last_error(void);
 
 /* Table ids for tree_attn_plan_export (all int32, row-major). */
 enum {
-  TA_T_PARAMS = 0,        /* [24]: version, n_nodes, n_queries, qpl, n_qheads, n_kvheads,
+  TA_T_PARAMS = 0,        /* [26]: version, n_nodes, n_queries, qpl, n_qheads, n_kvheads,
                              head_dim, page_size, ts_q, ts_c, gamma, rb, waves, floor_f, ncu,
                              split, forced, chunk_align, n_groups, n_chunks, n_items, n_slots,
-                             c_glob, n_runs */
+                             c_glob, n_runs, stream_rows, n_stream_items */
   TA_T_EDGES = 1,         /* [n_nodes] f(parent -> v), 0 at the root */
   TA_T_NQ = 2,            /* [n_nodes] queries left in v's virtual node */
   TA_T_LCUM = 3,          /* [n_nodes] cumulative context length after merging */
@@ -151,7 +153,8 @@ enum {
   TA_T_GROUP_QS = 5,      /* [sum n_q] query ids per group, ascending */
   TA_T_GROUP_VIS = 6,     /* [sum n_q] visible segment prefix per group query */
   TA_T_CHUNKS = 7,        /* [n_chunks x 3] group, tok0, tok1 (segment positions) */
-  TA_T_ITEMS = 8,         /* [n_items x 4] group, row0, nrows, chunk; launch order */
+  TA_T_ITEMS = 8,         /* [n_items x 5] group, row0, nrows, chunk, class (1 = workgroup
+                             item, 0 = single-wave item); launch order, workgroup items first */
   TA_T_Q_SLOT_PTR = 9,    /* [n_queries + 1] */
   TA_T_Q_SLOTS = 10,      /* partial slots of each query, root side first, chunks ascending */
   TA_T_RUNS = 11,         /* [n_runs x 3] page id, first slot, tokens */

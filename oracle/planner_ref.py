@@ -25,8 +25,11 @@ with the reasons in the design notes):
   SplitQCost  = C_P(nQ_curr - nQ_l, len_v) + C_P(nQ_l, len_l + len_v);
   C_P = C_{P,q} + C_{P,c}; the common factor d is dropped; Pad(TS, 0) = 0.
 * Constants (not printed on the page): TS_q = 16, TS_c = 64, gamma = 32.
-* Split rule, row blocks, work-item order, slot numbering and page runs are
-  this library's own, written out step by step below.
+* Split rule, row blocks, work-item classes and order, slot numbering and
+  page runs are this library's own, written out step by step below. Groups
+  with at most ``stream_rows`` rows become single-wave stream items (one row
+  block); larger groups become workgroup items (row blocks of ``rb``) whose
+  four waves share the chunk. The split rule counts capacity in waves.
 
 Parity unpinned: the constants and the split rule (the page prints no plan,
 no cost value and no threshold); they are pinned only against this file.
@@ -37,7 +40,8 @@ from collections import deque
 
 import numpy as np
 
-FORMAT_VERSION = 1
+FORMAT_VERSION = 2
+WAVES_PER_WG = 4
 CHUNK_ALIGN = 16
 ITEM_FIXED_COST = 256
 
@@ -47,7 +51,8 @@ T_PARAMS, T_EDGES, T_NQ, T_LCUM, T_GROUPS, T_GROUP_QS, T_GROUP_VIS, T_CHUNKS, T_
 TABLE_NAMES = ["params", "edges", "nq", "lcum", "groups", "group_qs", "group_vis", "chunks",
                "items", "q_slot_ptr", "q_slots", "runs", "chunk_run_ptr", "bfs"]
 
-DEFAULTS = dict(ts_q=16, ts_c=64, gamma=32, rb=256, waves=4, floor_f=4, ncu=256, split=1)
+DEFAULTS = dict(ts_q=16, ts_c=64, gamma=32, rb=256, waves=8, floor_f=4, ncu=256, split=1,
+                stream_rows=16)
 
 
 class PlanError(ValueError):
@@ -99,6 +104,7 @@ def build_plan(parent, node_len, node_page_ptr, node_page_ids, page_size, qpl,
             o[k] = int(v)
     if "split" in opts:
         o["split"] = int(opts["split"])
+    o["stream_rows"] = max(0, o["stream_rows"])     # negative: no single-wave items
     ts_q, ts_c, gamma, rb = o["ts_q"], o["ts_c"], o["gamma"], o["rb"]
     parent = [int(x) for x in parent]
     lens = [int(x) for x in node_len]
@@ -236,11 +242,14 @@ def build_plan(parent, node_len, node_page_ptr, node_page_ids, page_size, qpl,
         groups.append(dict(node=v, top=top[v], kv_len=kv_len, qs=qs, vis=vis, seg=seg,
                            rows=len(qs) * g))
 
-    # ---- P6 / P7: row blocks and KV chunks
+    # ---- P6 / P7: item class, row blocks and KV chunks
     for G in groups:
-        G["nblocks"] = _cdiv(G["rows"], rb)
+        G["cls"] = 0 if G["rows"] <= o["stream_rows"] else 1   # 0 = stream (one wave), 1 = workgroup
+        G["nblocks"] = 1 if G["cls"] == 0 else _cdiv(G["rows"], rb)
+        G["rb"] = G["rows"] if G["cls"] == 0 else rb
     if o["split"]:
-        W = H * sum(G["nblocks"] * G["kv_len"] for G in groups)
+        W = H * sum((1 if G["cls"] == 0 else WAVES_PER_WG) * G["nblocks"] * G["kv_len"]
+                    for G in groups)
         U = _cdiv(W, o["ncu"] * o["waves"])
         c_glob = max(ts_c, _align_up(U, ts_c))
     else:
@@ -249,7 +258,7 @@ def build_plan(parent, node_len, node_page_ptr, node_page_ids, page_size, qpl,
     for gi, G in enumerate(groups):
         kvl = G["kv_len"]
         if o["split"]:
-            cg = max(c_glob, _align_up(o["floor_f"] * min(G["rows"], rb), ts_c))
+            cg = max(c_glob, _align_up(o["floor_f"] * min(G["rows"], G["rb"]), ts_c))
             nch = _cdiv(kvl, cg)
             csz = _align_up(_cdiv(kvl, nch), CHUNK_ALIGN)
             nch = _cdiv(kvl, csz)
@@ -260,17 +269,19 @@ def build_plan(parent, node_len, node_page_ptr, node_page_ids, page_size, qpl,
         for i in range(nch):
             chunks.append((gi, i * csz, min(kvl, (i + 1) * csz)))
 
-    # ---- P8: work items, longest first (stable on (group, block, chunk))
+    # ---- P8: work items: workgroup items first, then stream items; each
+    # class longest first (stable on (group, block, chunk))
     items = []
     for gi, G in enumerate(groups):
         for b in range(G["nblocks"]):
-            r0 = b * rb
-            nr = min(G["rows"], r0 + rb) - r0
+            r0 = b * G["rb"]
+            nr = min(G["rows"], r0 + G["rb"]) - r0
             for c in range(G["n_chunks"]):
                 ci = G["chunk_ptr"] + c
                 est = (chunks[ci][2] - chunks[ci][1]) * (ITEM_FIXED_COST + nr)
-                items.append((est, gi, r0, nr, ci))
-    items.sort(key=lambda t: -t[0])   # Python's sort is stable
+                items.append((est, gi, r0, nr, ci, G["cls"]))
+    items.sort(key=lambda t: (-t[5], -t[0]))   # Python's sort is stable
+    n_stream = sum(1 for t in items if t[5] == 0)
 
     # ---- P9: slots
     slot_base = 0
@@ -326,7 +337,7 @@ def build_plan(parent, node_len, node_page_ptr, node_page_ids, page_size, qpl,
     params = [FORMAT_VERSION, n, n_q, qpl, n_qheads, n_kvheads, head_dim, page_size,
               ts_q, ts_c, gamma, rb, o["waves"], o["floor_f"], o["ncu"], o["split"],
               1 if force_edges is not None else 0, CHUNK_ALIGN, len(groups), len(chunks),
-              len(items), n_slots, c_glob, len(runs)]
+              len(items), n_slots, c_glob, len(runs), o["stream_rows"], n_stream]
     gq, gv, gt = [], [], []
     for G in groups:
         gt.append([G["node"], G["top"], G["kv_len"], len(G["qs"]), len(gq), G["chunk_ptr"],
@@ -343,7 +354,7 @@ def build_plan(parent, node_len, node_page_ptr, node_page_ids, page_size, qpl,
         "group_qs": i32(gq),
         "group_vis": i32(gv),
         "chunks": i32([list(c) for c in chunks], (-1, 3)),
-        "items": i32([[t[1], t[2], t[3], t[4]] for t in items], (-1, 4)),
+        "items": i32([[t[1], t[2], t[3], t[4], t[5]] for t in items], (-1, 5)),
         "q_slot_ptr": i32(q_slot_ptr),
         "q_slots": i32(q_slots),
         "runs": i32(runs, (-1, 3)),

@@ -117,7 +117,7 @@ def check_invariants(inst, plan):
         assert (cs[1:, 1] == cs[:-1, 2]).all() and (cs[:, 2] > cs[:, 1]).all()
     # (4) items cover every (group, row, chunk) exactly once
     seen = set()
-    for gi_, r0, nr, ci in plan["items"]:
+    for gi_, r0, nr, ci, _cls in plan["items"]:
         assert chunks[ci, 0] == gi_
         for r in range(r0, r0 + nr):
             key = (int(gi_), r, int(ci))
@@ -125,6 +125,16 @@ def check_invariants(inst, plan):
             seen.add(key)
     total = sum(int(G[3]) * g * int(G[6]) for G in groups)
     assert len(seen) == total
+    # (4b) classes: single-wave items are groups of at most stream_rows rows, in
+    # one row block; workgroup items come first in launch order
+    srows = int(P[24])
+    cls = plan["items"][:, 4]
+    assert (np.diff(cls) <= 0).all() and int(P[25]) == int((cls == 0).sum())
+    for gi_, r0, nr, ci, c in plan["items"]:
+        rows_g = int(groups[gi_][3]) * g
+        assert c == (0 if rows_g <= srows else 1)
+        if c == 0:
+            assert r0 == 0 and nr == rows_g
     # (5) slots are a bijection onto (group, chunk, query-in-group)
     sl = plan["q_slots"]
     assert sorted(sl.tolist()) == list(range(int(P[21])))

@@ -15,7 +15,7 @@ TABLE_IDS = {
     "chunks": 7, "items": 8, "q_slot_ptr": 9, "q_slots": 10, "runs": 11, "chunk_run_ptr": 12,
     "bfs": 13,
 }
-TABLE_COLS = {"groups": 8, "chunks": 3, "items": 4, "runs": 3}
+TABLE_COLS = {"groups": 8, "chunks": 3, "items": 5, "runs": 3}
 
 EXPORTED_SYMBOLS = [
     "tree_attn_plan", "tree_attn_decode", "tree_attn_plan_info", "tree_attn_plan_export",
@@ -31,6 +31,7 @@ class PlanOpts(ctypes.Structure):
         ("ncu", ctypes.c_int32), ("no_split", ctypes.c_int32),
         ("force_edges", ctypes.POINTER(ctypes.c_int8)), ("host_only", ctypes.c_int32),
         ("scale", ctypes.c_float), ("poison_workspace", ctypes.c_int32),
+        ("stream_rows", ctypes.c_int32),
     ]
 
 

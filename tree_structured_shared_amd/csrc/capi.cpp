@@ -84,8 +84,8 @@ ta_status upload(ta_plan* p) {
   // work items in launch order
   std::vector<ta::WorkItem> items(T.n_items);
   for (int32_t x = 0; x < T.n_items; ++x) {
-    const int32_t gi = T.items[4 * x], r0 = T.items[4 * x + 1], nr = T.items[4 * x + 2],
-                  ci = T.items[4 * x + 3];
+    const int32_t gi = T.items[5 * x], r0 = T.items[5 * x + 1], nr = T.items[5 * x + 2],
+                  ci = T.items[5 * x + 3];
     const int32_t* G = &T.groups[8 * gi];
     ta::WorkItem w{};
     w.q_ptr = G[4];
@@ -172,6 +172,7 @@ ta_status tree_attn_plan(const int32_t* parent, int32_t n_nodes, const int32_t* 
       poison = opts->poison_workspace ? 1 : 0;
       scale = opts->scale;
       if (opts->ncu) pp.ncu = opts->ncu;
+      if (opts->stream_rows) pp.stream_rows = opts->stream_rows < 0 ? 0 : opts->stream_rows;
     }
     int device = -1;
     if (!host_only) {
@@ -278,8 +279,8 @@ ta_status tree_attn_decode(const void* q, ta_dtype q_dtype, const ta_paged_kv* k
   a.n_kvheads = plan->n_kvheads;
   a.g = plan->g;
   a.scale_log2 = plan->scale * 1.4426950408889634f;
-  e = ta::launch_partial(a, plan->T.n_items * plan->n_kvheads, q_dtype == TA_BF16 ? 1 : 0,
-                         plan->head_dim, s);
+  e = ta::launch_partial(a, plan->T.n_items - plan->T.n_stream_items, plan->T.n_stream_items,
+                         q_dtype == TA_BF16 ? 1 : 0, plan->head_dim, s);
   if (e != hipSuccess) return hip_err(e, "tree_attn_decode: partial-attention launch");
   if (timed && (e = hipEventRecord(mp->ev[3 * mp->timing_n + 1], s)) != hipSuccess)
     return hip_err(e, "tree_attn_decode: hipEventRecord");

@@ -47,8 +47,10 @@ struct ReduceArgs {
 };
 
 // dtype: 0 = fp32, 1 = bf16 (Q, K and V share it).
-hipError_t launch_partial(const PartialArgs& a, int32_t n_work, int dtype, int head_dim,
-                          hipStream_t s);
+// Items [0, n_block_items) run one workgroup per item x kv-head; the next
+// n_wave_items run one wave per item x kv-head.
+hipError_t launch_partial(const PartialArgs& a, int32_t n_block_items, int32_t n_wave_items, int dtype,
+                          int head_dim, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_fill(float* p, int64_t n, float value, hipStream_t s);
 

@@ -15,11 +15,15 @@
 //      common factor d dropped, Pad(TS, 0) = 0).
 //  P5  one group per virtual node with queries left (DeFT notes, KV-guided
 //      split: a node's KV grouped with every query that shares it).
-//  P6  row blocks of at most rb rows; row r = (query r / g, q-head r % g).
+//  P6  item class and row blocks: a group with at most stream_rows rows is
+//      one single-wave stream block; a larger one is cut into workgroup
+//      blocks of at most rb rows. Row r = (query r / g, q-head r % g).
 //  P7  long-context split (FastTree review, section 3.3): a global chunk
-//      length sized so the launch gives about ncu * waves workgroups, floored
-//      per group at floor_f tokens per row, balanced and 16-aligned.
-//  P8  work items ordered longest first (stable).
+//      length sized so the launch gives about ncu * waves busy waves (a
+//      workgroup block counts its four waves), floored per group at floor_f
+//      tokens per row, balanced and 16-aligned.
+//  P8  work items: workgroup items first, then stream items, each class
+//      longest first (stable).
 //  P9  partial-result slots: group, then chunk, then query.
 //  P10 page runs of every chunk and the per-token page table the kernel reads.
 #include "planner.h"
@@ -42,6 +46,7 @@ inline int64_t pad_cost(int64_t nq, int64_t len, int64_t ts_q, int64_t ts_c) {
 
 struct Group {
   int32_t node, top, kv_len, rows, nblocks, chunk_ptr, n_chunks, slot_base, q_ptr, seg_base;
+  int32_t cls, rb;  // cls 0 = stream (one wave), 1 = workgroup
   std::vector<int32_t> qs, vis, seg;
 };
 
@@ -67,7 +72,7 @@ int build_plan(const int32_t* parent, int32_t n, const int32_t* node_len,
   if (page_size < 1 || page_size > 256)
     return fail(err, EINVAL_, "tree_attn_plan: page_size must be in 1..256");
   if (p.ts_q < 1 || p.ts_c < 1 || p.gamma < 0 || p.rb < 1 || p.waves < 1 || p.floor_f < 0 ||
-      p.ncu < 1)
+      p.ncu < 1 || p.stream_rows < 0)
     return fail(err, EINVAL_, "tree_attn_plan: invalid option value");
   int32_t root = -1;
   for (int32_t v = 0; v < n; ++v) {
@@ -204,11 +209,15 @@ int build_plan(const int32_t* parent, int32_t n, const int32_t* node_len,
   }
 
   // ---- P6 / P7
-  for (auto& G : groups) G.nblocks = int32_t(cdiv(G.rows, p.rb));
+  for (auto& G : groups) {
+    G.cls = G.rows <= p.stream_rows ? 0 : 1;
+    G.nblocks = G.cls == 0 ? 1 : int32_t(cdiv(G.rows, p.rb));
+    G.rb = G.cls == 0 ? G.rows : p.rb;
+  }
   int64_t c_glob = 0;
   if (p.split) {
     int64_t W = 0;
-    for (auto& G : groups) W += int64_t(G.nblocks) * G.kv_len;
+    for (auto& G : groups) W += int64_t(G.cls == 0 ? 1 : kWavesPerWG) * G.nblocks * G.kv_len;
     W *= H;
     const int64_t U = cdiv(W, int64_t(p.ncu) * p.waves);
     c_glob = std::max<int64_t>(p.ts_c, align_up(U, p.ts_c));
@@ -220,7 +229,7 @@ int build_plan(const int32_t* parent, int32_t n, const int32_t* node_len,
     int64_t csz, nch;
     if (p.split) {
       const int64_t cg =
-          std::max<int64_t>(c_glob, align_up(int64_t(p.floor_f) * std::min(G.rows, p.rb), p.ts_c));
+          std::max<int64_t>(c_glob, align_up(int64_t(p.floor_f) * std::min(G.rows, G.rb), p.ts_c));
       nch = cdiv(G.kv_len, cg);
       csz = align_up(cdiv(G.kv_len, nch), kChunkAlign);
       nch = cdiv(G.kv_len, csz);
@@ -235,20 +244,26 @@ int build_plan(const int32_t* parent, int32_t n, const int32_t* node_len,
   }
 
   // ---- P8 items (longest first; stable on natural order)
-  struct Item { int64_t est; int32_t group, row0, nrows, chunk; };
+  struct Item { int64_t est; int32_t group, row0, nrows, chunk, cls; };
   std::vector<Item> items;
   for (int32_t gi = 0; gi < int32_t(groups.size()); ++gi) {
     const Group& G = groups[gi];
     for (int32_t b = 0; b < G.nblocks; ++b) {
-      const int32_t r0 = b * p.rb;
-      const int32_t nr = std::min(G.rows, r0 + p.rb) - r0;
+      const int32_t r0 = b * G.rb;
+      const int32_t nr = std::min(G.rows, r0 + G.rb) - r0;
       for (int32_t c = 0; c < G.n_chunks; ++c) {
         const Chunk& C = chunks[G.chunk_ptr + c];
-        items.push_back({int64_t(C.t1 - C.t0) * (kItemFixedCost + nr), gi, r0, nr, G.chunk_ptr + c});
+        items.push_back(
+            {int64_t(C.t1 - C.t0) * (kItemFixedCost + nr), gi, r0, nr, G.chunk_ptr + c, G.cls});
       }
     }
   }
-  std::stable_sort(items.begin(), items.end(), [](const Item& a, const Item& b) { return a.est > b.est; });
+  std::stable_sort(items.begin(), items.end(), [](const Item& a, const Item& b) {
+    if (a.cls != b.cls) return a.cls > b.cls;
+    return a.est > b.est;
+  });
+  int32_t n_stream = 0;
+  for (const Item& I : items) n_stream += I.cls == 0 ? 1 : 0;
 
   // ---- P9 slots
   int32_t slot = 0;
@@ -329,7 +344,8 @@ int build_plan(const int32_t* parent, int32_t n, const int32_t* node_len,
   T.params = {kFormatVersion, n, n_q, qpl, n_qheads, n_kvheads, head_dim, page_size,
               p.ts_q, p.ts_c, p.gamma, p.rb, p.waves, p.floor_f, p.ncu, p.split ? 1 : 0,
               p.force_edges ? 1 : 0, kChunkAlign, int32_t(groups.size()), int32_t(chunks.size()),
-              int32_t(items.size()), n_slots, int32_t(c_glob), int32_t(T.runs.size() / 3)};
+              int32_t(items.size()), n_slots, int32_t(c_glob), int32_t(T.runs.size() / 3),
+              p.stream_rows, n_stream};
   T.edges = f;
   T.nq = nQ;
   T.lcum.assign(n, 0);
@@ -342,7 +358,7 @@ int build_plan(const int32_t* parent, int32_t n, const int32_t* node_len,
     T.group_vis.insert(T.group_vis.end(), G.vis.begin(), G.vis.end());
   }
   for (const Chunk& C : chunks) T.chunks.insert(T.chunks.end(), {C.group, C.t0, C.t1});
-  for (const Item& I : items) T.items.insert(T.items.end(), {I.group, I.row0, I.nrows, I.chunk});
+  for (const Item& I : items) T.items.insert(T.items.end(), {I.group, I.row0, I.nrows, I.chunk, I.cls});
   T.q_slot_ptr.push_back(0);
   for (int32_t q = 0; q < n_q; ++q) {
     T.q_slots.insert(T.q_slots.end(), qsl[q].begin(), qsl[q].end());
@@ -353,6 +369,7 @@ int build_plan(const int32_t* parent, int32_t n, const int32_t* node_len,
   T.n_groups = int32_t(groups.size());
   T.n_chunks = int32_t(chunks.size());
   T.n_items = int32_t(items.size());
+  T.n_stream_items = n_stream;
   T.n_slots = n_slots;
   T.max_page_id = max_page;
   return 0;

@@ -9,15 +9,17 @@
 namespace ta {
 
 struct PlanParams {
-  int32_t ts_q = 16, ts_c = 64, gamma = 32, rb = 256, waves = 4, floor_f = 4, ncu = 256;
+  int32_t ts_q = 16, ts_c = 64, gamma = 32, rb = 256, waves = 8, floor_f = 4, ncu = 256;
   int32_t split = 1;
+  int32_t stream_rows = 16;  // groups with at most this many rows run as one-wave items
   const int8_t* force_edges = nullptr;
 };
 
-constexpr int32_t kFormatVersion = 1;
+constexpr int32_t kFormatVersion = 2;
+constexpr int32_t kWavesPerWG = 4;     // waves of a workgroup item
 constexpr int32_t kChunkAlign = 16;     // chunk lengths are multiples of the MFMA token block
 constexpr int64_t kItemFixedCost = 256; // per-item cost proxy in row units (longest-first order)
-constexpr int32_t kParamsLen = 24;
+constexpr int32_t kParamsLen = 26;
 
 struct PlanTables {
   // exported (see include/tree_attn.h for the layouts)
@@ -27,6 +29,7 @@ struct PlanTables {
   std::vector<int32_t> seg_tok;        // per group segment: (page_id << 8) | slot, one per token
   std::vector<int32_t> group_seg_base; // offset of each group's segment in seg_tok
   int32_t n_queries = 0, n_groups = 0, n_chunks = 0, n_items = 0, n_slots = 0;
+  int32_t n_stream_items = 0;  // items [n_items - n_stream_items, n_items) are one-wave items
   int32_t max_page_id = -1;
 };
 
