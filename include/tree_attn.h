@@ -59,7 +59,7 @@ typedef struct {
   int32_t ts_q;    /* query tile of the padding cost (default 16) */
   int32_t ts_c;    /* context tile of the padding cost and chunk alignment (default 64) */
   int32_t gamma;   /* intermediate-result cost per query, in token units (default 32) */
-  int32_t rb;      /* maximum rows (query x q-head-in-group) per work item (default 256) */
+  int32_t rb;      /* maximum rows (query x q-head-in-group) per work item (default 128) */
   int32_t waves;   /* target busy waves per CU for the split rule (default 8) */
   int32_t floor_f; /* chunk length floor, in tokens per row (default 4) */
   int32_t ncu;     /* compute units (default: the current device's count; 256 if host_only) */

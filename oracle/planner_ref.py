@@ -51,7 +51,7 @@ T_PARAMS, T_EDGES, T_NQ, T_LCUM, T_GROUPS, T_GROUP_QS, T_GROUP_VIS, T_CHUNKS, T_
 TABLE_NAMES = ["params", "edges", "nq", "lcum", "groups", "group_qs", "group_vis", "chunks",
                "items", "q_slot_ptr", "q_slots", "runs", "chunk_run_ptr", "bfs"]
 
-DEFAULTS = dict(ts_q=16, ts_c=64, gamma=32, rb=256, waves=8, floor_f=4, ncu=256, split=1,
+DEFAULTS = dict(ts_q=16, ts_c=64, gamma=32, rb=128, waves=8, floor_f=4, ncu=256, split=1,
                 stream_rows=16)
 
 
@@ -245,8 +245,12 @@ def build_plan(parent, node_len, node_page_ptr, node_page_ids, page_size, qpl,
     # ---- P6 / P7: item class, row blocks and KV chunks
     for G in groups:
         G["cls"] = 0 if G["rows"] <= o["stream_rows"] else 1   # 0 = stream (one wave), 1 = workgroup
-        G["nblocks"] = 1 if G["cls"] == 0 else _cdiv(G["rows"], rb)
-        G["rb"] = G["rows"] if G["cls"] == 0 else rb
+        if G["cls"] == 0:
+            G["nblocks"], G["rb"] = 1, G["rows"]
+        else:   # balanced blocks of at most rb rows, 16-aligned when rb is
+            nb = _cdiv(G["rows"], rb)
+            G["rb"] = _align_up(_cdiv(G["rows"], nb), 16 if rb % 16 == 0 else 1)
+            G["nblocks"] = _cdiv(G["rows"], G["rb"])
     if o["split"]:
         W = H * sum((1 if G["cls"] == 0 else WAVES_PER_WG) * G["nblocks"] * G["kv_len"]
                     for G in groups)

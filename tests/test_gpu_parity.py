@@ -179,3 +179,35 @@ def test_timing_records():
     pm, rm = plan.timing_read(4)
     assert len(pm) == 3 and (pm > 0).all() and (rm > 0).all()
     plan.close()
+
+
+def test_graph_capture_replays():
+    """A decode captured in a HIP graph (through torch's graph capture; the
+    plan forks its workgroup items onto a side stream and joins back) replays
+    to the eager result, with eager decodes and synchronisations between the
+    replays."""
+    inst = synth.make_config(5)
+    q, k, v = _dev(inst)
+    plan = Plan.for_instance(inst)
+    eager = plan.decode(q, k, v).clone()
+    torch.cuda.synchronize()
+    out = torch.empty_like(eager)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        plan.decode(q, k, v, out=out)        # warm-up on the capture stream
+        side.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            plan.decode(q, k, v, out=out)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep}"
+        other = plan.decode(q, k, v)          # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(other, eager)
+    plan.close()

@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstring>
 #include <new>
@@ -42,6 +44,10 @@ struct ta_plan {
   float *d_o_part = nullptr, *d_m_part = nullptr, *d_l_part = nullptr;
   int64_t ws_bytes = 0;
   std::vector<hipEvent_t> ev;  // 3 per timed decode
+  // side stream: workgroup items run there while single-wave items run on
+  // the caller's stream (fork and join through two events, default priority)
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
   int32_t timing_cap = 0, timing_n = 0;
 };
 
@@ -72,6 +78,11 @@ void free_device(ta_plan* p) {
   if (p->host_only) return;
   for (hipEvent_t e : p->ev) (void)hipEventDestroy(e);
   p->ev.clear();
+  if (p->fork) (void)hipEventDestroy(p->fork);
+  if (p->join) (void)hipEventDestroy(p->join);
+  if (p->side) (void)hipStreamDestroy(p->side);
+  p->fork = p->join = nullptr;
+  p->side = nullptr;
   if (p->d_tables) (void)hipFree(p->d_tables);
   if (p->d_ws) (void)hipFree(p->d_ws);
   p->d_tables = p->d_ws = nullptr;
@@ -81,6 +92,12 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 ta_status upload(ta_plan* p) {
   const ta::PlanTables& T = p->T;
+  // visible tokens of each query over its whole path (sum over its groups)
+  std::vector<int64_t> q_vis(T.n_queries, 0);
+  for (int32_t gi = 0; gi < T.n_groups; ++gi) {
+    const int32_t* G = &T.groups[8 * gi];
+    for (int32_t x = 0; x < G[3]; ++x) q_vis[T.group_qs[G[4] + x]] += T.group_vis[G[4] + x];
+  }
   // work items in launch order
   std::vector<ta::WorkItem> items(T.n_items);
   for (int32_t x = 0; x < T.n_items; ++x) {
@@ -95,6 +112,10 @@ ta_status upload(ta_plan* p) {
     w.tok1 = T.chunks[3 * ci + 2];
     w.seg_base = T.group_seg_base[gi];
     w.slot0 = G[7] + (ci - G[5]) * G[3];
+    int64_t min_vis = INT64_MAX;
+    for (int32_t qig = r0 / p->g; qig <= (r0 + nr - 1) / p->g; ++qig)
+      min_vis = std::min(min_vis, q_vis[T.group_qs[G[4] + qig]]);
+    w.flags = min_vis < ta::kHiLoMinPath ? 1 : 0;
     items[x] = w;
   }
   const size_t sz_items = items.size() * sizeof(ta::WorkItem);
@@ -134,6 +155,12 @@ ta_status upload(ta_plan* p) {
   if (e != hipSuccess) {
     p->d_ws = nullptr;
     return set_err(TA_ENOMEM, std::string("tree_attn_plan: hipMalloc(workspace): ") + hipGetErrorString(e));
+  }
+  if (T.n_stream_items > 0 && T.n_stream_items < T.n_items) {
+    if ((e = hipStreamCreateWithFlags(&p->side, hipStreamNonBlocking)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&p->fork, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&p->join, hipEventDisableTiming)) != hipSuccess)
+      return hip_err(e, "tree_attn_plan: side stream");
   }
   uint8_t* wb = static_cast<uint8_t*>(p->d_ws);
   p->d_o_part = reinterpret_cast<float*>(wb);
@@ -272,6 +299,14 @@ ta_status tree_attn_decode(const void* q, ta_dtype q_dtype, const ta_paged_kv* k
   a.stride_page = kv->stride_page;
   a.stride_token = kv->stride_token;
   a.stride_head = kv->stride_head;
+  {
+    const int64_t es = (q_dtype == TA_BF16) ? 2 : 4;
+    a.sp_bytes = kv->stride_page * es;
+    a.st_bytes = kv->stride_token * es;
+    const int64_t max_off = ((kv->n_pages - 1) * kv->stride_page + (kv->page_size - 1) * kv->stride_token +
+                             int64_t(plan->n_kvheads - 1) * kv->stride_head + plan->head_dim) * es;
+    a.fast_addr = (max_off < (int64_t(1) << 32) && a.sp_bytes < (1 << 24) && a.st_bytes < (1 << 24)) ? 1 : 0;
+  }
   a.o_part = plan->d_o_part;
   a.m_part = plan->d_m_part;
   a.l_part = plan->d_l_part;
@@ -279,9 +314,23 @@ ta_status tree_attn_decode(const void* q, ta_dtype q_dtype, const ta_paged_kv* k
   a.n_kvheads = plan->n_kvheads;
   a.g = plan->g;
   a.scale_log2 = plan->scale * 1.4426950408889634f;
-  e = ta::launch_partial(a, plan->T.n_items - plan->T.n_stream_items, plan->T.n_stream_items,
-                         q_dtype == TA_BF16 ? 1 : 0, plan->head_dim, s);
-  if (e != hipSuccess) return hip_err(e, "tree_attn_decode: partial-attention launch");
+  const int dt = q_dtype == TA_BF16 ? 1 : 0;
+  const int32_t n_block = plan->T.n_items - plan->T.n_stream_items, n_wave = plan->T.n_stream_items;
+  if (n_block > 0 && n_wave > 0) {
+    if ((e = hipEventRecord(plan->fork, s)) != hipSuccess || (e = hipStreamWaitEvent(plan->side, plan->fork, 0)) != hipSuccess)
+      return hip_err(e, "tree_attn_decode: fork");
+    if ((e = ta::launch_block_items(a, n_block, dt, plan->head_dim, plan->side)) != hipSuccess)
+      return hip_err(e, "tree_attn_decode: workgroup-item launch");
+    if ((e = ta::launch_wave_items(a, n_block, n_wave, dt, plan->head_dim, s)) != hipSuccess)
+      return hip_err(e, "tree_attn_decode: single-wave-item launch");
+    if ((e = hipEventRecord(plan->join, plan->side)) != hipSuccess || (e = hipStreamWaitEvent(s, plan->join, 0)) != hipSuccess)
+      return hip_err(e, "tree_attn_decode: join");
+  } else {
+    if ((e = ta::launch_block_items(a, n_block, dt, plan->head_dim, s)) != hipSuccess)
+      return hip_err(e, "tree_attn_decode: workgroup-item launch");
+    if ((e = ta::launch_wave_items(a, n_block, n_wave, dt, plan->head_dim, s)) != hipSuccess)
+      return hip_err(e, "tree_attn_decode: single-wave-item launch");
+  }
   if (timed && (e = hipEventRecord(mp->ev[3 * mp->timing_n + 1], s)) != hipSuccess)
     return hip_err(e, "tree_attn_decode: hipEventRecord");
 

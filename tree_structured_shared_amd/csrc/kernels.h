@@ -17,8 +17,14 @@ struct WorkItem {
   int32_t tok1;      // chunk end (exclusive)
   int32_t seg_base;  // offset of the group's segment in seg_tok
   int32_t slot0;     // slot of the chunk's first group query: slot_base + chunk * n_q
-  int32_t pad;
+  int32_t flags;     // bit 0: P enters P V as a bf16 hi + lo pair (some query of the
+                     // item sees fewer than kHiLoMinPath tokens in total)
 };
+
+// Below this many visible tokens (over a query's whole path) the rounding of
+// the softmax weights to bf16 before the P V product is no longer averaged
+// away, so such queries get the exact two-term (hi + lo) product.
+constexpr int32_t kHiLoMinPath = 1024;
 
 struct PartialArgs {
   const WorkItem* items;
@@ -29,6 +35,9 @@ struct PartialArgs {
   const void* k;
   const void* v;
   int64_t stride_page, stride_token, stride_head;  // elements
+  int64_t sp_bytes, st_bytes;   // page and token strides in bytes
+  int32_t fast_addr;            // 1: every pool byte offset fits 32 bits and both
+                                // byte strides fit 24 bits (24-bit multiplies)
   float* o_part;   // [n_slots, n_qheads, D] unnormalised
   float* m_part;   // [n_slots, n_qheads] running max, base-2 scaled units
   float* l_part;   // [n_slots, n_qheads] sum of exp2(s - m)
@@ -47,10 +56,13 @@ struct ReduceArgs {
 };
 
 // dtype: 0 = fp32, 1 = bf16 (Q, K and V share it).
-// Items [0, n_block_items) run one workgroup per item x kv-head; the next
-// n_wave_items run one wave per item x kv-head.
-hipError_t launch_partial(const PartialArgs& a, int32_t n_block_items, int32_t n_wave_items, int dtype,
-                          int head_dim, hipStream_t s);
+// Items [0, n_block_items) run one workgroup per item x kv-head; items
+// [item0, item0 + n_wave_items) run one wave per item x kv-head. The two
+// launches touch disjoint partial slots and may run concurrently.
+hipError_t launch_block_items(const PartialArgs& a, int32_t n_block_items, int dtype, int head_dim,
+                              hipStream_t s);
+hipError_t launch_wave_items(const PartialArgs& a, int32_t item0, int32_t n_wave_items, int dtype,
+                             int head_dim, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_fill(float* p, int64_t n, float value, hipStream_t s);
 

@@ -1,28 +1,31 @@
 // HIP kernels for tree-structured decode attention on CDNA4 (gfx950).
 //
-// Partial attention: a work item is one KV chunk of one context-query group
-// and a block of its rows (row = query x q-head-in-group); its kernel streams
-// the chunk's paged K/V once for all those rows -- the KV-guided grouping of the DeFT reading notes and the
-// single-launch, one-group-per-block-set kernel of the FastTree review
-// (section 3, kernel design) -- and runs a flash-style online softmax over it
-// (DeFT notes, attention calculation; FastTree review, tile-by-tile online
-// softmax). It writes one unnormalised partial (m, l, o) per row. Groups with
-// few rows run as single-wave items (wave_items_kernel: every wave of the
-// launch is an independent item x kv-head); groups with many rows run as
-// workgroup items (block_items_kernel: one item x kv-head per workgroup, the
-// four waves split rows, or rows and tokens).
+// Partial attention. A work item is one KV chunk of one context-query group
+// and a block of its rows (row = query x q-head-in-group). The item's chunk of
+// paged K/V is streamed once for all its rows -- the KV-guided grouping of the
+// DeFT reading notes and the single-launch kernel of the FastTree review
+// (section 3, kernel design: every group dispatched to its own blocks of one
+// launch) -- with a flash-style online softmax over 32-token tiles (DeFT
+// notes, attention calculation; FastTree review, tile-by-tile online softmax).
+// Each row ends in one unnormalised partial (m, l, o) in the workspace.
 //
+// Every wave works alone: no LDS and no barrier anywhere in partial attention.
+//  * wave_items_kernel: groups with few rows. Each wave of the launch is one
+//    item x kv-head.
+//  * block_items_kernel: groups with many rows. One workgroup per item x
+//    kv-head; wave w owns row tiles w and w+4 of the block (128 rows per
+//    workgroup) and streams the whole chunk for them (the four waves read the
+//    same chunk, so three of them hit in cache).
 // Two row paths, chosen per item by its row count (the review's multi-stage
 // query tiling: small tiles near the leaves, large ones near the root):
-//  * GEMV-sized items (few rows, or fp32 inputs): wavefront dot products with
-//    8 lanes per token, xor-shuffle reductions, and per-lane online softmax.
-//  * GEMM-sized items (bf16): v_mfma_f32_16x16x32_bf16 on a transposed
-//    formulation -- S^T = K Q^T (K rows are the A operand, loaded straight
-//    from the paged pool) and O^T = V^T P^T, where the score accumulator
-//    layout is already the B-operand layout of P, and V^T comes from an 8x8
-//    register transpose of 16-byte V loads (stacking queries that share KV
-//    turns the decode GEMV into a GEMM, FastTree review, kernel design).
-//    No LDS and no barrier in the streaming loop: every wave runs alone.
+//  * GEMV-sized items (one or two rows, and every fp32 item): wavefront dot
+//    products, 8 lanes per token, DPP reductions, per-lane online softmax.
+//  * GEMM-sized bf16 items: v_mfma_f32_16x16x32_bf16 on a transposed
+//    formulation. S^T = K Q^T: K rows are the A operand, loaded straight from
+//    the pool. O^T = V^T P^T: the score accumulators already sit in the
+//    B-operand layout of P^T, and V^T comes from a v_perm transpose of 16-byte
+//    V loads (stacking the queries that share KV turns the decode GEMV into a
+//    GEMM, FastTree review, kernel design).
 //
 // lse_reduce: per (query, q-head), merges that query's partials along its
 // path (root-side group first, chunks ascending) by log-sum-exp -- the
@@ -30,8 +33,8 @@
 //
 // Softmax runs in base 2: scores are scaled by scale * log2(e) and the
 // workspace m is in those units. The running max is only raised when a new
-// score exceeds it by more than 8 (in log2 units), so rescaling is rare; the
-// stored (m, l, o) stay consistent because l and o are always relative to m.
+// score exceeds it by more than 8 (log2 units), so rescaling is rare; l and o
+// always stay relative to the stored m.
 #include "kernels.h"
 
 #include <type_traits>
@@ -46,7 +49,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBlock = 256;
 constexpr int kWaves = 4;
-constexpr int kValuMaxRows = 4;   // bf16 items with more rows take the MFMA path
+constexpr int kValuMaxRows = 2;   // bf16 items with more rows take the MFMA path
+constexpr int kBlockRowTiles = 2; // 16-row tiles per wave in workgroup items
 constexpr float kRescale = 8.0f;  // lazy-rescale threshold, log2 units
 #define TA_NEG_INF (-__builtin_inff())
 
@@ -55,42 +59,76 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-__device__ __forceinline__ int64_t tok_off(int32_t st, const PartialArgs& a) {
-  return int64_t(st >> 8) * a.stride_page + int64_t(st & 255) * a.stride_token;
+// Byte offset of a pool token from its page-table entry (page << 8 | slot).
+// FA: every offset fits 32 bits and both byte strides fit 24 bits, so two
+// full-rate 24-bit multiplies do it and loads take the uniform-base +
+// 32-bit-offset addressing form.
+template <bool FA>
+struct TokOff;
+template <>
+struct TokOff<true> {
+  typedef uint32_t type;
+  static __device__ __forceinline__ uint32_t of(int32_t st, const PartialArgs& a) {
+    return __umul24(uint32_t(st) >> 8, uint32_t(a.sp_bytes)) + __umul24(uint32_t(st) & 255u, uint32_t(a.st_bytes));
+  }
+};
+template <>
+struct TokOff<false> {
+  typedef int64_t type;
+  static __device__ __forceinline__ int64_t of(int32_t st, const PartialArgs& a) {
+    return int64_t(st >> 8) * a.sp_bytes + int64_t(st & 255) * a.st_bytes;
+  }
+};
+
+template <typename V, typename O>
+__device__ __forceinline__ V load_at(const char* base, O off) {
+  return *reinterpret_cast<const V*>(base + off);
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane helpers (VALU only: DPP and the gfx950 permlane swaps).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// all-reduce sum over each aligned group of 8 lanes: quad_perm xor 1, xor 2,
+// then row_half_mirror pairs the two quads of the group
+__device__ __forceinline__ float sum8(float v) {
+  v += dpp_mov<0xB1>(v);
+  v += dpp_mov<0x4E>(v);
+  v += dpp_mov<0x141>(v);
+  return v;
+}
+// value of lane l ^ 8 (row_ror:8 inside each 16-lane row)
+__device__ __forceinline__ float xor8(float v) { return dpp_mov<0x128>(v); }
+// value of lane l ^ 16 / l ^ 32: each permlane swap returns the pair
+// (x[l & ~16], x[l | 16]) (resp. 32) in lane l
+__device__ __forceinline__ float xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+// max / sum over lanes l, l^16, l^32, l^48
+__device__ __forceinline__ float max4rows(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum4rows(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // weight of a partial with max m against a combined max M (0 for empty parts)
 __device__ __forceinline__ float part_weight(float m, float M) {
   return (m == TA_NEG_INF) ? 0.0f : fast_exp2(m - M);
 }
-
-// ---------------------------------------------------------------------------
-// raw per-lane slices of EPL elements, loaded as 16-byte words
-template <typename T, int EPL>
-struct Slice {
-  static constexpr int kWords = EPL * int(sizeof(T)) / 16;
-  u32x4 w[kWords];
-  __device__ __forceinline__ void load(const T* p) {
-#pragma unroll
-    for (int c = 0; c < kWords; ++c) w[c] = *reinterpret_cast<const u32x4*>(p + c * (16 / sizeof(T)));
-  }
-  __device__ __forceinline__ void to_float(float* out) const {
-    if constexpr (std::is_same<T, float>::value) {
-#pragma unroll
-      for (int c = 0; c < kWords; ++c)
-#pragma unroll
-        for (int x = 0; x < 4; ++x) out[4 * c + x] = __uint_as_float(w[c][x]);
-    } else {
-#pragma unroll
-      for (int c = 0; c < kWords; ++c)
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          out[8 * c + 2 * x] = bf_lo(w[c][x]);
-          out[8 * c + 2 * x + 1] = bf_hi(w[c][x]);
-        }
-    }
-  }
-};
 
 // ---------------------------------------------------------------------------
 // Rows of a work item. Row rr of the item is group row row0 + rr = (group
@@ -113,11 +151,42 @@ __device__ __forceinline__ RowRef row_ref(const PartialArgs& a, const WorkItem& 
   return r;
 }
 
+__device__ __forceinline__ const char* pool_head(const void* pool, const PartialArgs& a, int h, int esize) {
+  return reinterpret_cast<const char*>(pool) + int64_t(h) * a.stride_head * esize;
+}
+
 // ---------------------------------------------------------------------------
 // GEMV path: up to R rows. A wave streams tokens with 8 lanes per token (each
 // lane owns D/8 consecutive head-dim elements) and 2 tokens per 8-lane group
 // per step; every 8-lane group keeps its own online-softmax state, merged
 // across the wave at the end.
+template <typename T, int EPL>
+struct Slice {  // EPL elements of one token row, as 16-byte words
+  static constexpr int kWords = EPL * int(sizeof(T)) / 16;
+  u32x4 w[kWords];
+  template <typename O>
+  __device__ __forceinline__ void load(const char* base, O off) {
+#pragma unroll
+    for (int c = 0; c < kWords; ++c) w[c] = load_at<u32x4>(base, off + O(16 * c));
+  }
+  __device__ __forceinline__ void to_float(float* out) const {
+    if constexpr (std::is_same<T, float>::value) {
+#pragma unroll
+      for (int c = 0; c < kWords; ++c)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) out[4 * c + x] = __uint_as_float(w[c][x]);
+    } else {
+#pragma unroll
+      for (int c = 0; c < kWords; ++c)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          out[8 * c + 2 * x] = bf_lo(w[c][x]);
+          out[8 * c + 2 * x + 1] = bf_hi(w[c][x]);
+        }
+    }
+  }
+};
+
 template <typename T, int D, int R>
 struct ValuState {
   static constexpr int EPL = D / 8;
@@ -131,7 +200,7 @@ __device__ __forceinline__ void valu_init(ValuState<T, D, R>& S, const PartialAr
                                           int h, int rbeg) {
   constexpr int EPL = D / 8;
   const int e = threadIdx.x & 7;
-  const T* qbase = reinterpret_cast<const T*>(a.q);
+  const char* qbase = reinterpret_cast<const char*>(a.q);
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     S.row[r] = row_ref(a, it, h, rbeg + r);
@@ -144,105 +213,127 @@ __device__ __forceinline__ void valu_init(ValuState<T, D, R>& S, const PartialAr
     }
     if (S.row[r].ok) {
       Slice<T, EPL> sq;
-      sq.load(qbase + (int64_t(S.row[r].gq) * a.n_qheads + S.row[r].qh) * D + e * EPL);
+      sq.load(qbase, ((int64_t(S.row[r].gq) * a.n_qheads + S.row[r].qh) * D + e * EPL) * int64_t(sizeof(T)));
       sq.to_float(S.q[r]);
     }
   }
 }
 
 template <typename T, int D, int R>
+__device__ __forceinline__ void valu_step(ValuState<T, D, R>& S, const Slice<T, D / 8> (&kc)[2],
+                                          const Slice<T, D / 8> (&vc)[2], const PartialArgs& a, int base,
+                                          int we, int tg) {
+  constexpr int EPL = D / 8;
+  float kf[2][EPL], vf[2][EPL];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    kc[u].to_float(kf[u]);
+    vc[u].to_float(vf[u]);
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float s[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) acc = __builtin_fmaf(S.q[r][k], kf[u][k], acc);
+      acc = sum8(acc);
+      const int t = base + u * 8 + tg;
+      s[u] = (t < we && t < S.row[r].vis) ? acc * a.scale_log2 : TA_NEG_INF;
+    }
+    const float smax = fmaxf(s[0], s[1]);
+    if (smax > S.m[r] + kRescale) {
+      const float al = part_weight(S.m[r], smax);
+      S.l[r] *= al;
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) S.o[r][k] *= al;
+      S.m[r] = smax;
+    }
+    const float p0 = (s[0] == TA_NEG_INF) ? 0.0f : fast_exp2(s[0] - S.m[r]);
+    const float p1 = (s[1] == TA_NEG_INF) ? 0.0f : fast_exp2(s[1] - S.m[r]);
+    S.l[r] += p0 + p1;
+#pragma unroll
+    for (int k = 0; k < EPL; ++k)
+      S.o[r][k] = __builtin_fmaf(p1, vf[1][k], __builtin_fmaf(p0, vf[0][k], S.o[r][k]));
+  }
+}
+
+// Steps of 16 tokens over [wb, we). Two buffers alternate with no register
+// copies, so the wait before each step's arithmetic covers only older loads:
+// page-table entries run one step ahead of K/V, K/V one step ahead of the
+// math. Loads past the end clamp to the last token (cache-resident, unused).
+template <typename T, int D, int R, bool FA>
 __device__ __forceinline__ void valu_stream(ValuState<T, D, R>& S, const PartialArgs& a,
                                             const WorkItem& it, int h, int wb, int we) {
+  typedef typename TokOff<FA>::type Off;
   constexpr int EPL = D / 8;
   if (wb >= we) return;
   const int lane = threadIdx.x & 63;
   const int tg = lane >> 3, e = lane & 7;
-  const T* kb = reinterpret_cast<const T*>(a.k) + int64_t(h) * a.stride_head + e * EPL;
-  const T* vb = reinterpret_cast<const T*>(a.v) + int64_t(h) * a.stride_head + e * EPL;
+  const char* kb = pool_head(a.k, a, h, sizeof(T));
+  const char* vb = pool_head(a.v, a, h, sizeof(T));
+  const Off lane_off = Off(e * EPL * int(sizeof(T)));
   const int32_t* st = a.seg_tok + it.seg_base;
-
-  Slice<T, EPL> kc[2], vc[2];
+  const int last = we - 1;
+  int32_t sA[2], sB[2];
+  Slice<T, EPL> kA[2], vA[2], kB[2], vB[2];
+  auto seg = [&](int32_t (&sg)[2], int b) {
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int64_t off = tok_off(st[min(wb + u * 8 + tg, we - 1)], a);
-    kc[u].load(kb + off);
-    vc[u].load(vb + off);
-  }
-  for (int base = wb; base < we; base += 16) {
-    Slice<T, EPL> kn[2], vn[2];
-    const int nb = base + 16;
-    if (nb < we) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int64_t off = tok_off(st[min(nb + u * 8 + tg, we - 1)], a);
-        kn[u].load(kb + off);
-        vn[u].load(vb + off);
-      }
-    }
-    float kf[2][EPL], vf[2][EPL];
+    for (int u = 0; u < 2; ++u) sg[u] = st[min(b + u * 8 + tg, last)];
+  };
+  auto kv = [&](Slice<T, EPL> (&kk)[2], Slice<T, EPL> (&vv)[2], const int32_t (&sg)[2]) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      kc[u].to_float(kf[u]);
-      vc[u].to_float(vf[u]);
+      const Off off = TokOff<FA>::of(sg[u], a) + lane_off;
+      kk[u].load(kb, off);
+      vv[u].load(vb, off);
     }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      float s[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int k = 0; k < EPL; ++k) acc = __builtin_fmaf(S.q[r][k], kf[u][k], acc);
-        acc += __shfl_xor(acc, 1, 64);
-        acc += __shfl_xor(acc, 2, 64);
-        acc += __shfl_xor(acc, 4, 64);
-        const int t = base + u * 8 + tg;
-        s[u] = (t < we && t < S.row[r].vis) ? acc * a.scale_log2 : TA_NEG_INF;
-      }
-      const float smax = fmaxf(s[0], s[1]);
-      if (smax > S.m[r] + kRescale) {
-        const float al = part_weight(S.m[r], smax);
-        S.l[r] *= al;
-#pragma unroll
-        for (int k = 0; k < EPL; ++k) S.o[r][k] *= al;
-        S.m[r] = smax;
-      }
-      const float p0 = (s[0] == TA_NEG_INF) ? 0.0f : fast_exp2(s[0] - S.m[r]);
-      const float p1 = (s[1] == TA_NEG_INF) ? 0.0f : fast_exp2(s[1] - S.m[r]);
-      S.l[r] += p0 + p1;
-#pragma unroll
-      for (int k = 0; k < EPL; ++k)
-        S.o[r][k] = __builtin_fmaf(p1, vf[1][k], __builtin_fmaf(p0, vf[0][k], S.o[r][k]));
-    }
-    if (nb < we) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        kc[u] = kn[u];
-        vc[u] = vn[u];
-      }
-    }
+  };
+  seg(sA, wb);
+  kv(kA, vA, sA);
+  seg(sB, wb + 16);
+  for (int base = wb; base < we; base += 32) {
+    kv(kB, vB, sB);
+    seg(sA, base + 32);
+    valu_step(S, kA, vA, a, base, we, tg);
+    if (base + 16 >= we) break;
+    kv(kA, vA, sA);
+    seg(sB, base + 48);
+    valu_step(S, kB, vB, a, base + 16, we, tg);
   }
 }
 
 // merge the 8 token groups of a wave (lanes e, e+8, ..., e+56); afterwards
 // every lane group holds the wave's state
-template <typename T, int D, int R>
-__device__ __forceinline__ void valu_merge_lanes(ValuState<T, D, R>& S) {
+template <int X>
+__device__ __forceinline__ float lane_xor(float v) {
+  if constexpr (X == 8) return xor8(v);
+  else if constexpr (X == 16) return xor16(v);
+  else return xor32(v);
+}
+
+template <int X, typename T, int D, int R>
+__device__ __forceinline__ void valu_merge_step(ValuState<T, D, R>& S) {
   constexpr int EPL = D / 8;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
+    const float mo = lane_xor<X>(S.m[r]);
+    const float lo = lane_xor<X>(S.l[r]);
+    const float M = fmaxf(S.m[r], mo);
+    const float as = part_weight(S.m[r], M), ao = part_weight(mo, M);
+    S.l[r] = S.l[r] * as + lo * ao;
 #pragma unroll
-    for (int x = 8; x < 64; x <<= 1) {
-      const float mo = __shfl_xor(S.m[r], x, 64);
-      const float lo = __shfl_xor(S.l[r], x, 64);
-      const float M = fmaxf(S.m[r], mo);
-      const float as = part_weight(S.m[r], M), ao = part_weight(mo, M);
-      S.l[r] = S.l[r] * as + lo * ao;
-#pragma unroll
-      for (int k = 0; k < EPL; ++k) S.o[r][k] = S.o[r][k] * as + __shfl_xor(S.o[r][k], x, 64) * ao;
-      S.m[r] = M;
-    }
+    for (int k = 0; k < EPL; ++k) S.o[r][k] = S.o[r][k] * as + lane_xor<X>(S.o[r][k]) * ao;
+    S.m[r] = M;
   }
+}
+
+template <typename T, int D, int R>
+__device__ __forceinline__ void valu_merge_lanes(ValuState<T, D, R>& S) {
+  valu_merge_step<8>(S);
+  valu_merge_step<16>(S);
+  valu_merge_step<32>(S);
 }
 
 template <typename T, int D, int R>
@@ -266,70 +357,14 @@ __device__ __forceinline__ void valu_write(const ValuState<T, D, R>& S, const Pa
   }
 }
 
-// single wave: rows [rbeg, rbeg + R) over the whole chunk, written directly
-template <typename T, int D, int R>
+// one wave: rows [rbeg, rbeg + R) over the whole chunk, written directly
+template <typename T, int D, int R, bool FA>
 __device__ __forceinline__ void valu_wave_item(const PartialArgs& a, const WorkItem& it, int h, int rbeg) {
   ValuState<T, D, R> S;
   valu_init(S, a, it, h, rbeg);
-  valu_stream(S, a, it, h, it.tok0, it.tok1);
+  valu_stream<T, D, R, FA>(S, a, it, h, it.tok0, it.tok1);
   valu_merge_lanes(S);
   valu_write(S, a);
-}
-
-// four waves split the chunk's tokens, merge through LDS, write
-template <typename T, int D, int R>
-__device__ void valu_block_item(const PartialArgs& a, const WorkItem& it, int h, int rbeg, float* lds) {
-  constexpr int EPL = D / 8;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int tg = lane >> 3, e = lane & 7;
-  ValuState<T, D, R> S;
-  valu_init(S, a, it, h, rbeg);
-  const int ntok = it.tok1 - it.tok0;
-  const int per = (((ntok + kWaves - 1) / kWaves) + 7) & ~7;
-  const int wb = it.tok0 + wave * per;
-  valu_stream(S, a, it, h, wb, min(it.tok1, wb + per));
-  valu_merge_lanes(S);
-  // [wave][r][D + 2]
-  constexpr int RS = D + 2;
-  if (tg == 0) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      float* row = lds + (wave * R + r) * RS;
-#pragma unroll
-      for (int k = 0; k < EPL; ++k) row[e * EPL + k] = S.o[r][k];
-      if (e == 0) {
-        row[D] = S.m[r];
-        row[D + 1] = S.l[r];
-      }
-    }
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < R * D; idx += kBlock) {
-    const int r = idx / D, d = idx - (idx / D) * D;
-    RowRef rf{0, 0, 0, 0, false};
-#pragma unroll
-    for (int x = 0; x < R; ++x)
-      if (x == r) rf = S.row[x];
-    if (!rf.ok) continue;
-    float M = TA_NEG_INF;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, lds[(w * R + r) * RS + D]);
-    float acc = 0.0f, lsum = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float* row = lds + (w * R + r) * RS;
-      const float wgt = (M == TA_NEG_INF) ? 0.0f : part_weight(row[D], M);
-      acc += row[d] * wgt;
-      lsum += row[D + 1] * wgt;
-    }
-    const int64_t pi = int64_t(rf.slot) * a.n_qheads + rf.qh;
-    a.o_part[pi * D + d] = acc;
-    if (d == 0) {
-      a.m_part[pi] = M;
-      a.l_part[pi] = lsum;
-    }
-  }
-  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
@@ -340,17 +375,19 @@ __device__ void valu_block_item(const PartialArgs& a, const WorkItem& it, int h,
 __device__ __forceinline__ int tau(int j, int e) { return (e < 4) ? 4 * j + e : 16 + 4 * j + (e - 4); }
 
 template <int DPL>
-struct VSlice;  // DPL bf16 values of one token, V^T operand source
+struct VSlice;  // DPL bf16 values of one token (V^T operand source)
 template <>
 struct VSlice<8> {
   u32x4 w;
-  __device__ __forceinline__ void load(const __bf16* p) { w = *reinterpret_cast<const u32x4*>(p); }
+  template <typename O>
+  __device__ __forceinline__ void load(const char* base, O off) { w = load_at<u32x4>(base, off); }
   __device__ __forceinline__ uint32_t word(int x) const { return w[x]; }
 };
 template <>
 struct VSlice<4> {
   u32x2 w;
-  __device__ __forceinline__ void load(const __bf16* p) { w = *reinterpret_cast<const u32x2*>(p); }
+  template <typename O>
+  __device__ __forceinline__ void load(const char* base, O off) { w = load_at<u32x2>(base, off); }
   __device__ __forceinline__ uint32_t word(int x) const { return w[x]; }
 };
 
@@ -361,7 +398,8 @@ struct MfmaState {
   f32x4 O[NRTW][DPL];
   float m[NRTW], l[NRTW];
   RowRef row[NRTW];
-  bool on[NRTW];  // wave-uniform: row tile k exists
+  int vmin[NRTW];  // wave-uniform: smallest visible length over the tile's valid rows
+  bool on[NRTW];   // wave-uniform: row tile k exists
 };
 
 // row tile k of this wave covers item rows (rt[k] * 16 + i)
@@ -384,6 +422,13 @@ __device__ __forceinline__ void mfma_init(MfmaState<D, NRTW>& S, const PartialAr
     for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
       for (int x = 0; x < 8; ++x) S.qf[k][kk][x] = __bf16(0.0f);
+    {
+      // over the 16 rows of the tile (lanes i; the 4 lanes of a row agree)
+      float v = S.row[k].ok ? float(S.row[k].vis) : 3.0e38f;
+#pragma unroll
+      for (int x = 1; x < 16; x <<= 1) v = fminf(v, __shfl_xor(v, x, 64));
+      S.vmin[k] = __builtin_amdgcn_readfirstlane(int(fminf(v, 2.0e9f)));
+    }
     if (S.row[k].ok) {
       const __bf16* qp = qbase + (int64_t(S.row[k].gq) * a.n_qheads + S.row[k].qh) * D + j * 8;
 #pragma unroll
@@ -392,141 +437,183 @@ __device__ __forceinline__ void mfma_init(MfmaState<D, NRTW>& S, const PartialAr
   }
 }
 
-// stream 32-token tiles kt = kt0, kt0 + kstep, ... of the item's chunk
-template <int D, int NRTW>
-__device__ __forceinline__ void mfma_stream(MfmaState<D, NRTW>& S, const PartialArgs& a, const WorkItem& it,
-                                            int h, int kt0, int kstep) {
+// page-table entries of one 32-token tile: the lane's two K tokens and its
+// eight V tokens (clamped to the chunk's last token past its end)
+struct TileSeg {
+  int32_t k[2], v[8];
+};
+
+__device__ __forceinline__ void load_tile_seg(TileSeg& t, const int32_t* st, int base, int last, int i, int j) {
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) t.k[tb] = st[min(base + tb * 16 + i, last)];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) t.v[e] = st[min(base + tau(j, e), last)];
+}
+
+// one 32-token K/V tile in MFMA operand order
+template <int D>
+struct TileKV {
+  u32x4 k[2][D / 32];
+  VSlice<D / 16> v[8];
+};
+
+template <int D, bool FA>
+__device__ __forceinline__ void load_tile_kv(TileKV<D>& b, const TileSeg& sg, const char* kb, const char* vb,
+                                             int j, int i, const PartialArgs& a) {
+  typedef typename TokOff<FA>::type Off;
+  constexpr int DPL = D / 16;
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    const Off off = TokOff<FA>::of(sg.k[tb], a) + Off(j * 16);
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) b.k[tb][kk] = load_at<u32x4>(kb, off + Off(kk * 64));
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) b.v[e].load(vb, TokOff<FA>::of(sg.v[e], a) + Off(i * DPL * 2));
+}
+
+// softmax of one row tile's 32 scores and their P V product.
+// FULL: every token of the tile is visible to every row (no mask, and the
+// running max is finite afterwards, so no -inf guard). hilo (wave-uniform):
+// P = P_hi + P_lo, both bf16, so the product keeps ~16 mantissa bits of P;
+// otherwise P is rounded once to bf16 and l sums the rounded weights, so the
+// output stays an exact weighted average of V.
+template <int D, int NRTW, bool FULL>
+__device__ __forceinline__ void mfma_softmax_pv(MfmaState<D, NRTW>& S, int k, const f32x4& s0, const f32x4& s1,
+                                                const bf16x8 (&vt)[D / 16], float c, int lim, int j, bool hilo) {
+  constexpr int DPL = D / 16;
+  float sv[8];
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    sv[x] = s0[x];
+    sv[4 + x] = s1[x];
+  }
+  if constexpr (!FULL) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      if (4 * j + x >= lim) sv[x] = TA_NEG_INF;
+      if (16 + 4 * j + x >= lim) sv[4 + x] = TA_NEG_INF;
+    }
+  }
+  float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+  mx = max4rows(mx) * c;  // c > 0: the max of scaled scores
+  if (mx > S.m[k] + kRescale) {
+    const float al = part_weight(S.m[k], mx);
+    S.l[k] *= al;
+#pragma unroll
+    for (int db = 0; db < DPL; ++db) S.O[k][db] *= al;
+    S.m[k] = mx;
+  }
+  const float nm = -S.m[k];
+  bf16x8 pb;
+  float p[8];
+  float psum_r = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    p[e] = fast_exp2(__builtin_fmaf(sv[e], c, nm));
+    if constexpr (!FULL) p[e] = (sv[e] == TA_NEG_INF) ? 0.0f : p[e];
+    pb[e] = __bf16(p[e]);
+    psum_r += float(pb[e]);
+  }
+  if (hilo) {
+    bf16x8 pl;
+    float psum = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      psum += p[e];
+      pl[e] = __bf16(p[e] - float(pb[e]));
+    }
+    S.l[k] += psum;
+#pragma unroll
+    for (int db = 0; db < DPL; ++db) {
+      S.O[k][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[db], pb, S.O[k][db], 0, 0, 0);
+      S.O[k][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[db], pl, S.O[k][db], 0, 0, 0);
+    }
+  } else {
+    S.l[k] += psum_r;
+#pragma unroll
+    for (int db = 0; db < DPL; ++db)
+      S.O[k][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[db], pb, S.O[k][db], 0, 0, 0);
+  }
+}
+
+// FAST: take the mask-free softmax when the whole tile is visible (worth
+// its extra code in compute-heavy workgroup items only).
+template <int D, int NRTW, bool FAST>
+__device__ __forceinline__ void mfma_tile(MfmaState<D, NRTW>& S, const TileKV<D>& b, const PartialArgs& a,
+                                          const WorkItem& it, int base, int j) {
   constexpr int KK = D / 32, DPL = D / 16;
+  // V^T operands: A_db element e = V[tau(j, e)][DPL * i + db]; v_perm picks
+  // the low (db even) or high (db odd) halves of two token words
+  bf16x8 vt[DPL];
+#pragma unroll
+  for (int db = 0; db < DPL; ++db) {
+    const uint32_t sel = (db & 1) ? 0x07060302u : 0x05040100u;
+    u32x4 wv;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      wv[u] = __builtin_amdgcn_perm(b.v[2 * u + 1].word(db >> 1), b.v[2 * u].word(db >> 1), sel);
+    vt[db] = __builtin_bit_cast(bf16x8, wv);
+  }
+  const bool hilo = it.flags & 1;
+#pragma unroll
+  for (int k = 0; k < NRTW; ++k) {
+    if (!S.on[k]) continue;
+    f32x4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b.k[0][kk]), S.qf[k][kk], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b.k[1][kk]), S.qf[k][kk], s1, 0, 0, 0);
+    }
+    const int lim = min(it.tok1, S.row[k].vis) - base;  // visible tokens of this tile: [0, lim)
+    if (FAST && base + 32 <= min(it.tok1, S.vmin[k]))  // wave-uniform
+      mfma_softmax_pv<D, NRTW, true>(S, k, s0, s1, vt, a.scale_log2, lim, j, hilo);
+    else
+      mfma_softmax_pv<D, NRTW, false>(S, k, s0, s1, vt, a.scale_log2, lim, j, hilo);
+  }
+}
+
+// Stream the item's 32-token tiles. Two tile buffers alternate with no
+// register copies (as in valu_stream): while tile n is computed, tile n + 1's
+// K/V and tile n + 2's page-table entries are in flight.
+template <int D, int NRTW, bool FA, bool FAST>
+__device__ __forceinline__ void mfma_stream(MfmaState<D, NRTW>& S, const PartialArgs& a, const WorkItem& it,
+                                            int h) {
   const int lane = threadIdx.x & 63;
   const int i = lane & 15, j = lane >> 4;
   const int ntiles = (it.tok1 - it.tok0 + 31) >> 5;
-  if (kt0 >= ntiles) return;
-  const __bf16* kb = reinterpret_cast<const __bf16*>(a.k) + int64_t(h) * a.stride_head + j * 8;
-  const __bf16* vb = reinterpret_cast<const __bf16*>(a.v) + int64_t(h) * a.stride_head + i * DPL;
+  const char* kb = pool_head(a.k, a, h, 2);
+  const char* vb = pool_head(a.v, a, h, 2);
   const int32_t* st = a.seg_tok + it.seg_base;
   const int last = it.tok1 - 1;
 
-  u32x4 kc[2][KK];
-  VSlice<DPL> vc[8];
-  {
-    const int base = it.tok0 + kt0 * 32;
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      const int64_t off = tok_off(st[min(base + tb * 16 + i, last)], a);
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) kc[tb][kk] = *reinterpret_cast<const u32x4*>(kb + off + kk * 32);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) vc[e].load(vb + tok_off(st[min(base + tau(j, e), last)], a));
-  }
-  for (int kt = kt0; kt < ntiles; kt += kstep) {
-    const int base = it.tok0 + kt * 32;
-    const int nbase = base + kstep * 32;
-    const bool more = kt + kstep < ntiles;
-    u32x4 kn[2][KK];
-    VSlice<DPL> vn[8];
-    if (more) {
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        const int64_t off = tok_off(st[min(nbase + tb * 16 + i, last)], a);
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) kn[tb][kk] = *reinterpret_cast<const u32x4*>(kb + off + kk * 32);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vn[e].load(vb + tok_off(st[min(nbase + tau(j, e), last)], a));
-    }
-
-    // V^T operands: A_db element e = V[tau(j, e)][DPL * i + db]
-    bf16x8 vt[DPL];
-#pragma unroll
-    for (int db = 0; db < DPL; ++db) {
-      u32x4 wv;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t x0 = vc[2 * u].word(db >> 1), x1 = vc[2 * u + 1].word(db >> 1);
-        wv[u] = (db & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
-      }
-      vt[db] = __builtin_bit_cast(bf16x8, wv);
-    }
-
-#pragma unroll
-    for (int k = 0; k < NRTW; ++k) {
-      if (!S.on[k]) continue;
-      f32x4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc[0][kk]), S.qf[k][kk], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc[1][kk]), S.qf[k][kk], s1, 0, 0, 0);
-      }
-      float sv[8];
-      const int vis = S.row[k].vis;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int t0 = base + 4 * j + c, t1 = base + 16 + 4 * j + c;
-        sv[c] = (t0 < it.tok1 && t0 < vis) ? s0[c] * a.scale_log2 : TA_NEG_INF;
-        sv[4 + c] = (t1 < it.tok1 && t1 < vis) ? s1[c] * a.scale_log2 : TA_NEG_INF;
-      }
-      float mx = sv[0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      if (mx > S.m[k] + kRescale) {
-        const float al = part_weight(S.m[k], mx);
-        S.l[k] *= al;
-#pragma unroll
-        for (int db = 0; db < DPL; ++db) S.O[k][db] *= al;
-        S.m[k] = mx;
-      }
-      // P = P_hi + P_lo, both bf16: the product keeps ~16 mantissa bits of P
-      // (a single bf16 P would cost up to 2^-9 relative per weight, visible
-      // when a query sees only a few tokens).
-      bf16x8 pb, pl;
-      float psum = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = (sv[e] == TA_NEG_INF) ? 0.0f : fast_exp2(sv[e] - S.m[k]);
-        psum += p;
-        const __bf16 hi = __bf16(p);
-        pb[e] = hi;
-        pl[e] = __bf16(p - float(hi));
-      }
-      S.l[k] += psum;
-#pragma unroll
-      for (int db = 0; db < DPL; ++db) {
-        S.O[k][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[db], pb, S.O[k][db], 0, 0, 0);
-        S.O[k][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[db], pl, S.O[k][db], 0, 0, 0);
-      }
-    }
-
-    if (more) {
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) kc[tb][kk] = kn[tb][kk];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vc[e] = vn[e];
-    }
+  TileSeg sgA, sgB;
+  TileKV<D> bA, bB;
+  int base = it.tok0;
+  load_tile_seg(sgA, st, base, last, i, j);
+  load_tile_kv<D, FA>(bA, sgA, kb, vb, j, i, a);
+  load_tile_seg(sgB, st, base + 32, last, i, j);
+  for (int kt = 0; kt < ntiles; kt += 2, base += 64) {
+    load_tile_kv<D, FA>(bB, sgB, kb, vb, j, i, a);
+    load_tile_seg(sgA, st, base + 64, last, i, j);
+    mfma_tile<D, NRTW, FAST>(S, bA, a, it, base, j);
+    if (kt + 1 >= ntiles) break;
+    load_tile_kv<D, FA>(bA, sgA, kb, vb, j, i, a);
+    load_tile_seg(sgB, st, base + 96, last, i, j);
+    mfma_tile<D, NRTW, FAST>(S, bB, a, it, base + 32, j);
   }
 }
 
-// l is lane-partial (its 8 tokens per tile); sum over the row's 4 lanes
+// lane (i, j) holds O[row i][d = DPL * (4j + c) + db] = O[k][db][c]; l is
+// lane-partial (its 8 tokens per tile) and is summed over the row's 4 lanes
 template <int D, int NRTW>
-__device__ __forceinline__ void mfma_finish(MfmaState<D, NRTW>& S) {
-#pragma unroll
-  for (int k = 0; k < NRTW; ++k) {
-    S.l[k] += __shfl_xor(S.l[k], 16, 64);
-    S.l[k] += __shfl_xor(S.l[k], 32, 64);
-  }
-}
-
-// lane (i, j) holds O[row i][d = DPL * (4j + c) + db] = O[k][db][c]
-template <int D, int NRTW>
-__device__ __forceinline__ void mfma_write(const MfmaState<D, NRTW>& S, const PartialArgs& a) {
+__device__ __forceinline__ void mfma_write(MfmaState<D, NRTW>& S, const PartialArgs& a) {
   constexpr int DPL = D / 16;
   const int j = (threadIdx.x & 63) >> 4;
 #pragma unroll
   for (int k = 0; k < NRTW; ++k) {
+    if (!S.on[k]) continue;
+    const float l = sum4rows(S.l[k]);
     if (!S.row[k].ok) continue;
     const int64_t pi = int64_t(S.row[k].slot) * a.n_qheads + S.row[k].qh;
     float* op = a.o_part + pi * D + 4 * j * DPL;
@@ -542,90 +629,58 @@ __device__ __forceinline__ void mfma_write(const MfmaState<D, NRTW>& S, const Pa
     }
     if (j == 0) {
       a.m_part[pi] = S.m[k];
-      a.l_part[pi] = S.l[k];
+      a.l_part[pi] = l;
     }
   }
 }
 
-// workgroup item, bf16: rows [16 * rt_base, ...) in nrt_pass row tiles. With
-// few tiles the waves also split the tokens (WT > 1) and merge through LDS.
-template <int D, int NRTW>
-__device__ void mfma_block_pass(const PartialArgs& a, const WorkItem& it, int h, int rt_base, int nrt_pass,
-                                float* lds) {
-  constexpr int DPL = D / 16;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int i = lane & 15, j = lane >> 4;
-  const int WR = (nrt_pass <= 1) ? 1 : (nrt_pass <= 2) ? 2 : 4;
-  const int WT = kWaves / WR;
-  const int wr = wave % WR, wt = wave / WR;
-  int rt[NRTW];
-  bool on[NRTW];
-#pragma unroll
-  for (int k = 0; k < NRTW; ++k) {
-    on[k] = wr + k * WR < nrt_pass;
-    rt[k] = rt_base + wr + k * WR;
-  }
+template <int D, int NRTW, bool FA, bool FAST>
+__device__ __forceinline__ void mfma_wave(const PartialArgs& a, const WorkItem& it, int h, const int (&rt)[NRTW],
+                                          const bool (&on)[NRTW]) {
   MfmaState<D, NRTW> S;
   mfma_init(S, a, it, h, rt, on);
-  mfma_stream(S, a, it, h, wt, WT);
-  mfma_finish(S);
-
-  constexpr int RS = D + 2;
-  if (WT > 1) {  // then each wave has one row tile (k = 0)
-    if (wt > 0 && S.on[0]) {
-      float* buf = lds + ((wt - 1) * WR + wr) * 16 * RS + i * RS;
-#pragma unroll
-      for (int db = 0; db < DPL; ++db)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) buf[DPL * (4 * j + c) + db] = S.O[0][db][c];
-      if (j == 0) {
-        buf[D] = S.m[0];
-        buf[D + 1] = S.l[0];
-      }
-    }
-    __syncthreads();
-    if (wt == 0 && S.on[0]) {
-      for (int w2 = 1; w2 < WT; ++w2) {
-        const float* buf = lds + ((w2 - 1) * WR + wr) * 16 * RS + i * RS;
-        const float mo = buf[D], lo = buf[D + 1];
-        const float M = fmaxf(S.m[0], mo);
-        const float as = part_weight(S.m[0], M), ao = part_weight(mo, M);
-        S.l[0] = S.l[0] * as + lo * ao;
-#pragma unroll
-        for (int db = 0; db < DPL; ++db)
-#pragma unroll
-          for (int c = 0; c < 4; ++c) S.O[0][db][c] = S.O[0][db][c] * as + buf[DPL * (4 * j + c) + db] * ao;
-        S.m[0] = M;
-      }
-    }
-    __syncthreads();
-  }
-  if (wt == 0) mfma_write(S, a);
+  mfma_stream<D, NRTW, FA, FAST>(S, a, it, h);
+  mfma_write(S, a);
 }
 
 // ---------------------------------------------------------------------------
-// Workgroup items (groups with many rows): one workgroup per item x kv-head.
-template <typename T, int D>
+// Workgroup items (groups with many rows): one workgroup per item x kv-head;
+// wave w owns row tiles w, w+4 (bf16) or row pairs (fp32).
+template <typename T, int D, bool FA>
 __global__ __launch_bounds__(kBlock) void block_items_kernel(PartialArgs a) {
-  __shared__ float lds[3 * 16 * (D + 2)];
   const int item = blockIdx.x / a.n_kvheads;
   const int h = blockIdx.x - item * a.n_kvheads;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const WorkItem it = a.items[item];
   if constexpr (std::is_same<T, __bf16>::value) {
     const int nrt = (it.nrows + 15) >> 4;
+    if (wave >= nrt) return;
     if (nrt <= 4) {
-      mfma_block_pass<D, 1>(a, it, h, 0, nrt, lds);
+      const int rt1[1] = {wave};
+      const bool on1[1] = {true};
+      mfma_wave<D, 1, FA, true>(a, it, h, rt1, on1);
     } else {
-      for (int rb = 0; rb < nrt; rb += 8) mfma_block_pass<D, 2>(a, it, h, rb, min(8, nrt - rb), lds);
+      // up to kBlockRowTiles row tiles per wave; rows beyond them take
+      // further passes (the planner's row blocks keep this to one pass)
+      for (int r0 = 0; r0 < nrt; r0 += kWaves * kBlockRowTiles) {
+        int rt[kBlockRowTiles];
+        bool on[kBlockRowTiles];
+#pragma unroll
+        for (int k = 0; k < kBlockRowTiles; ++k) {
+          rt[k] = r0 + wave + kWaves * k;
+          on[k] = rt[k] < nrt;
+        }
+        if (on[0]) mfma_wave<D, kBlockRowTiles, FA, true>(a, it, h, rt, on);
+      }
     }
   } else {
-    for (int r = 0; r < it.nrows; r += 4) valu_block_item<T, D, 4>(a, it, h, r, lds);
+    for (int r = 2 * wave; r < it.nrows; r += 2 * kWaves) valu_wave_item<T, D, 2, FA>(a, it, h, r);
   }
 }
 
 // Single-wave items (groups with few rows): each wave of the launch is one
-// item x kv-head and streams its whole chunk alone -- no LDS, no barrier.
-template <typename T, int D>
+// item x kv-head and streams its whole chunk alone.
+template <typename T, int D, bool FA>
 __global__ __launch_bounds__(kBlock, 2) void wave_items_kernel(PartialArgs a, int item0, int n_units) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int unit = blockIdx.x * kWaves + wave;
@@ -635,22 +690,16 @@ __global__ __launch_bounds__(kBlock, 2) void wave_items_kernel(PartialArgs a, in
   const WorkItem it = a.items[item];
   if constexpr (std::is_same<T, __bf16>::value) {
     if (it.nrows > kValuMaxRows) {
-      int rt[1] = {0};
-      bool on[1] = {true};
-      MfmaState<D, 1> S;
-      mfma_init(S, a, it, h, rt, on);
-      mfma_stream(S, a, it, h, 0, 1);
-      mfma_finish(S);
-      mfma_write(S, a);
+      const int rt[1] = {0};
+      const bool on[1] = {true};
+      mfma_wave<D, 1, FA, false>(a, it, h, rt, on);
       return;
     }
   }
   if (it.nrows <= 1) {
-    valu_wave_item<T, D, 1>(a, it, h, 0);
-  } else if (it.nrows <= 2) {
-    valu_wave_item<T, D, 2>(a, it, h, 0);
+    valu_wave_item<T, D, 1, FA>(a, it, h, 0);
   } else {
-    for (int r = 0; r < it.nrows; r += 4) valu_wave_item<T, D, 4>(a, it, h, r);
+    for (int r = 0; r < it.nrows; r += 2) valu_wave_item<T, D, 2, FA>(a, it, h, r);
   }
 }
 
@@ -707,36 +756,47 @@ __global__ void fill_kernel(float* p, int64_t n, float value) {
     p[x] = value;
 }
 
+template <typename T, int D>
+void launch_block_t(const PartialArgs& a, int32_t n_block_items, hipStream_t s) {
+  const dim3 grid(unsigned(n_block_items) * a.n_kvheads), block(kBlock);
+  if (a.fast_addr) hipLaunchKernelGGL((block_items_kernel<T, D, true>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((block_items_kernel<T, D, false>), grid, block, 0, s, a);
+}
+
+template <typename T, int D>
+void launch_wave_t(const PartialArgs& a, int32_t item0, int32_t n_wave_items, hipStream_t s) {
+  const int n_units = n_wave_items * a.n_kvheads;
+  const dim3 grid(unsigned((n_units + kWaves - 1) / kWaves)), block(kBlock);
+  if (a.fast_addr) hipLaunchKernelGGL((wave_items_kernel<T, D, true>), grid, block, 0, s, a, item0, n_units);
+  else hipLaunchKernelGGL((wave_items_kernel<T, D, false>), grid, block, 0, s, a, item0, n_units);
+}
+
 }  // namespace
 
-hipError_t launch_partial(const PartialArgs& a, int32_t n_block_items, int32_t n_wave_items, int dtype,
-                          int head_dim, hipStream_t s) {
-  const int H = a.n_kvheads;
-  if (n_block_items > 0) {
-    const dim3 grid(unsigned(n_block_items) * H), block(kBlock);
-    if (dtype == 1) {
-      if (head_dim == 128) hipLaunchKernelGGL((block_items_kernel<__bf16, 128>), grid, block, 0, s, a);
-      else hipLaunchKernelGGL((block_items_kernel<__bf16, 64>), grid, block, 0, s, a);
-    } else {
-      if (head_dim == 128) hipLaunchKernelGGL((block_items_kernel<float, 128>), grid, block, 0, s, a);
-      else hipLaunchKernelGGL((block_items_kernel<float, 64>), grid, block, 0, s, a);
-    }
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+hipError_t launch_block_items(const PartialArgs& a, int32_t n_block_items, int dtype, int head_dim,
+                              hipStream_t s) {
+  if (n_block_items <= 0) return hipSuccess;
+  if (dtype == 1) {
+    if (head_dim == 128) launch_block_t<__bf16, 128>(a, n_block_items, s);
+    else launch_block_t<__bf16, 64>(a, n_block_items, s);
+  } else {
+    if (head_dim == 128) launch_block_t<float, 128>(a, n_block_items, s);
+    else launch_block_t<float, 64>(a, n_block_items, s);
   }
-  if (n_wave_items > 0) {
-    const int n_units = n_wave_items * H;
-    const dim3 grid(unsigned((n_units + kWaves - 1) / kWaves)), block(kBlock);
-    if (dtype == 1) {
-      if (head_dim == 128) hipLaunchKernelGGL((wave_items_kernel<__bf16, 128>), grid, block, 0, s, a, n_block_items, n_units);
-      else hipLaunchKernelGGL((wave_items_kernel<__bf16, 64>), grid, block, 0, s, a, n_block_items, n_units);
-    } else {
-      if (head_dim == 128) hipLaunchKernelGGL((wave_items_kernel<float, 128>), grid, block, 0, s, a, n_block_items, n_units);
-      else hipLaunchKernelGGL((wave_items_kernel<float, 64>), grid, block, 0, s, a, n_block_items, n_units);
-    }
-    return hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_wave_items(const PartialArgs& a, int32_t item0, int32_t n_wave_items, int dtype,
+                             int head_dim, hipStream_t s) {
+  if (n_wave_items <= 0) return hipSuccess;
+  if (dtype == 1) {
+    if (head_dim == 128) launch_wave_t<__bf16, 128>(a, item0, n_wave_items, s);
+    else launch_wave_t<__bf16, 64>(a, item0, n_wave_items, s);
+  } else {
+    if (head_dim == 128) launch_wave_t<float, 128>(a, item0, n_wave_items, s);
+    else launch_wave_t<float, 64>(a, item0, n_wave_items, s);
   }
-  return hipSuccess;
+  return hipGetLastError();
 }
 
 hipError_t launch_reduce(const ReduceArgs& a, int head_dim, hipStream_t s) {

@@ -16,8 +16,9 @@
 //  P5  one group per virtual node with queries left (DeFT notes, KV-guided
 //      split: a node's KV grouped with every query that shares it).
 //  P6  item class and row blocks: a group with at most stream_rows rows is
-//      one single-wave stream block; a larger one is cut into workgroup
-//      blocks of at most rb rows. Row r = (query r / g, q-head r % g).
+//      one single-wave stream block; a larger one is cut into balanced
+//      workgroup blocks of at most rb rows (16-aligned when rb is). Row r =
+//      (query r / g, q-head r % g).
 //  P7  long-context split (FastTree review, section 3.3): a global chunk
 //      length sized so the launch gives about ncu * waves busy waves (a
 //      workgroup block counts its four waves), floored per group at floor_f
@@ -211,8 +212,14 @@ int build_plan(const int32_t* parent, int32_t n, const int32_t* node_len,
   // ---- P6 / P7
   for (auto& G : groups) {
     G.cls = G.rows <= p.stream_rows ? 0 : 1;
-    G.nblocks = G.cls == 0 ? 1 : int32_t(cdiv(G.rows, p.rb));
-    G.rb = G.cls == 0 ? G.rows : p.rb;
+    if (G.cls == 0) {
+      G.nblocks = 1;
+      G.rb = G.rows;
+    } else {  // balanced blocks of at most rb rows, 16-aligned when rb is
+      const int64_t nb = cdiv(G.rows, p.rb);
+      G.rb = int32_t(align_up(cdiv(G.rows, nb), p.rb % 16 == 0 ? 16 : 1));
+      G.nblocks = int32_t(cdiv(G.rows, G.rb));
+    }
   }
   int64_t c_glob = 0;
   if (p.split) {

@@ -9,7 +9,7 @@
 namespace ta {
 
 struct PlanParams {
-  int32_t ts_q = 16, ts_c = 64, gamma = 32, rb = 256, waves = 8, floor_f = 4, ncu = 256;
+  int32_t ts_q = 16, ts_c = 64, gamma = 32, rb = 128, waves = 8, floor_f = 4, ncu = 256;
   int32_t split = 1;
   int32_t stream_rows = 16;  // groups with at most this many rows run as one-wave items
   const int8_t* force_edges = nullptr;
