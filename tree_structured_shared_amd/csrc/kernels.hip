@@ -9,13 +9,13 @@
 // notes, attention calculation; FastTree review, tile-by-tile online softmax).
 // Each row ends in one unnormalised partial (m, l, o) in the workspace.
 //
-// Every wave works alone: no LDS and no barrier anywhere in partial attention.
 //  * wave_items_kernel: groups with few rows. Each wave of the launch is one
 //    item x kv-head.
-//  * block_items_kernel: groups with many rows. One workgroup per item x
-//    kv-head; wave w owns row tiles w and w+4 of the block (128 rows per
-//    workgroup) and streams the whole chunk for them (the four waves read the
-//    same chunk, so three of them hit in cache).
+//  * block_lds_kernel: groups with many rows (bf16). One workgroup per item
+//    x kv-head; the workgroup loads each K/V tile once into LDS (two stages,
+//    one barrier per tile) and wave w computes row tiles w and w+4 (128 rows
+//    per workgroup) from it. fp32 workgroup items (block_items_kernel) run
+//    the GEMV path per wave.
 // Two row paths, chosen per item by its row count (the review's multi-stage
 // query tiling: small tiles near the leaves, large ones near the root):
 //  * GEMV-sized items (one or two rows, and every fp32 item): wavefront dot
@@ -52,6 +52,10 @@ constexpr int kWaves = 4;
 constexpr int kValuMaxRows = 2;   // bf16 items with more rows take the MFMA path
 constexpr int kBlockRowTiles = 2; // 16-row tiles per wave in workgroup items
 constexpr float kRescale = 8.0f;  // lazy-rescale threshold, log2 units
+// initial running max of the MFMA path: finite, so exp2(s - m) of a masked
+// score (-inf) is 0 even before any score was seen, with no extra guard;
+// exp2(kMInit - anything finite) is 0, so the first real max replaces it.
+constexpr float kMInit = -1.0e30f;
 #define TA_NEG_INF (-__builtin_inff())
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -414,7 +418,7 @@ __device__ __forceinline__ void mfma_init(MfmaState<D, NRTW>& S, const PartialAr
   for (int k = 0; k < NRTW; ++k) {
     S.on[k] = on[k];
     S.row[k] = row_ref(a, it, h, on[k] ? rt[k] * 16 + i : it.nrows);
-    S.m[k] = TA_NEG_INF;
+    S.m[k] = kMInit;
     S.l[k] = 0.0f;
 #pragma unroll
     for (int db = 0; db < DPL; ++db) S.O[k][db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -472,23 +476,27 @@ __device__ __forceinline__ void load_tile_kv(TileKV<D>& b, const TileSeg& sg, co
   for (int e = 0; e < 8; ++e) b.v[e].load(vb, TokOff<FA>::of(sg.v[e], a) + Off(i * DPL * 2));
 }
 
-// softmax of one row tile's 32 scores and their P V product.
-// FULL: every token of the tile is visible to every row (no mask, and the
-// running max is finite afterwards, so no -inf guard). hilo (wave-uniform):
-// P = P_hi + P_lo, both bf16, so the product keeps ~16 mantissa bits of P;
-// otherwise P is rounded once to bf16 and l sums the rounded weights, so the
-// output stays an exact weighted average of V.
-template <int D, int NRTW, bool FULL>
-__device__ __forceinline__ void mfma_softmax_pv(MfmaState<D, NRTW>& S, int k, const f32x4& s0, const f32x4& s1,
-                                                const bf16x8 (&vt)[D / 16], float c, int lim, int j, bool hilo) {
+// softmax of one row tile's 32 scores: raises the running max when needed,
+// rescales l and O, and returns the weights as MFMA B operands. Tokens at or
+// past lim are masked (skipped, wave-uniformly, when the whole tile is
+// visible to every row of the tile). HILO: P = P_hi + P_lo,
+// both bf16, so the P V product keeps ~16 mantissa bits of P; otherwise P is
+// rounded once to bf16 and l sums the rounded weights, so the output stays
+// an exact weighted average of V.
+template <int D, int NRTW, bool HILO>
+__device__ __forceinline__ void mfma_softmax(MfmaState<D, NRTW>& S, int k, const f32x4& s0, const f32x4& s1,
+                                             const PartialArgs& a, const WorkItem& it, int base, int j,
+                                             bf16x8& pb, bf16x8& pl) {
   constexpr int DPL = D / 16;
+  const float c = a.scale_log2;
   float sv[8];
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
     sv[x] = s0[x];
     sv[4 + x] = s1[x];
   }
-  if constexpr (!FULL) {
+  if (base + 32 > min(it.tok1, S.vmin[k])) {  // wave-uniform: some token of the tile is masked
+    const int lim = min(it.tok1, S.row[k].vis) - base;
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       if (4 * j + x >= lim) sv[x] = TA_NEG_INF;
@@ -497,26 +505,24 @@ __device__ __forceinline__ void mfma_softmax_pv(MfmaState<D, NRTW>& S, int k, co
   }
   float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
   mx = max4rows(mx) * c;  // c > 0: the max of scaled scores
-  if (mx > S.m[k] + kRescale) {
-    const float al = part_weight(S.m[k], mx);
+  const bool raise = mx > S.m[k] + kRescale;
+  if (__builtin_amdgcn_ballot_w64(raise)) {  // rare after the first tiles
+    const float al = raise ? fast_exp2(S.m[k] - mx) : 1.0f;
     S.l[k] *= al;
 #pragma unroll
     for (int db = 0; db < DPL; ++db) S.O[k][db] *= al;
-    S.m[k] = mx;
+    S.m[k] = raise ? mx : S.m[k];
   }
   const float nm = -S.m[k];
-  bf16x8 pb;
   float p[8];
   float psum_r = 0.0f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     p[e] = fast_exp2(__builtin_fmaf(sv[e], c, nm));
-    if constexpr (!FULL) p[e] = (sv[e] == TA_NEG_INF) ? 0.0f : p[e];
     pb[e] = __bf16(p[e]);
     psum_r += float(pb[e]);
   }
-  if (hilo) {
-    bf16x8 pl;
+  if constexpr (HILO) {
     float psum = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -524,22 +530,20 @@ __device__ __forceinline__ void mfma_softmax_pv(MfmaState<D, NRTW>& S, int k, co
       pl[e] = __bf16(p[e] - float(pb[e]));
     }
     S.l[k] += psum;
-#pragma unroll
-    for (int db = 0; db < DPL; ++db) {
-      S.O[k][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[db], pb, S.O[k][db], 0, 0, 0);
-      S.O[k][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[db], pl, S.O[k][db], 0, 0, 0);
-    }
   } else {
     S.l[k] += psum_r;
-#pragma unroll
-    for (int db = 0; db < DPL; ++db)
-      S.O[k][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[db], pb, S.O[k][db], 0, 0, 0);
   }
 }
 
-// FAST: take the mask-free softmax when the whole tile is visible (worth
-// its extra code in compute-heavy workgroup items only).
-template <int D, int NRTW, bool FAST>
+// O^T[db] += V^T[db] P^T (and the lo half of P when hilo)
+template <int D, int NRTW, bool HILO>
+__device__ __forceinline__ void pv_update(MfmaState<D, NRTW>& S, int k, int db, const bf16x8& vt, const bf16x8& pb,
+                                          const bf16x8& pl) {
+  S.O[k][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pb, S.O[k][db], 0, 0, 0);
+  if constexpr (HILO) S.O[k][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pl, S.O[k][db], 0, 0, 0);
+}
+
+template <int D, int NRTW, bool HILO>
 __device__ __forceinline__ void mfma_tile(MfmaState<D, NRTW>& S, const TileKV<D>& b, const PartialArgs& a,
                                           const WorkItem& it, int base, int j) {
   constexpr int KK = D / 32, DPL = D / 16;
@@ -555,7 +559,6 @@ __device__ __forceinline__ void mfma_tile(MfmaState<D, NRTW>& S, const TileKV<D>
       wv[u] = __builtin_amdgcn_perm(b.v[2 * u + 1].word(db >> 1), b.v[2 * u].word(db >> 1), sel);
     vt[db] = __builtin_bit_cast(bf16x8, wv);
   }
-  const bool hilo = it.flags & 1;
 #pragma unroll
   for (int k = 0; k < NRTW; ++k) {
     if (!S.on[k]) continue;
@@ -565,18 +568,17 @@ __device__ __forceinline__ void mfma_tile(MfmaState<D, NRTW>& S, const TileKV<D>
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b.k[0][kk]), S.qf[k][kk], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b.k[1][kk]), S.qf[k][kk], s1, 0, 0, 0);
     }
-    const int lim = min(it.tok1, S.row[k].vis) - base;  // visible tokens of this tile: [0, lim)
-    if (FAST && base + 32 <= min(it.tok1, S.vmin[k]))  // wave-uniform
-      mfma_softmax_pv<D, NRTW, true>(S, k, s0, s1, vt, a.scale_log2, lim, j, hilo);
-    else
-      mfma_softmax_pv<D, NRTW, false>(S, k, s0, s1, vt, a.scale_log2, lim, j, hilo);
+    bf16x8 pb, pl;
+    mfma_softmax<D, NRTW, HILO>(S, k, s0, s1, a, it, base, j, pb, pl);
+#pragma unroll
+    for (int db = 0; db < DPL; ++db) pv_update<D, NRTW, HILO>(S, k, db, vt[db], pb, pl);
   }
 }
 
 // Stream the item's 32-token tiles. Two tile buffers alternate with no
 // register copies (as in valu_stream): while tile n is computed, tile n + 1's
 // K/V and tile n + 2's page-table entries are in flight.
-template <int D, int NRTW, bool FA, bool FAST>
+template <int D, int NRTW, bool FA, bool HILO>
 __device__ __forceinline__ void mfma_stream(MfmaState<D, NRTW>& S, const PartialArgs& a, const WorkItem& it,
                                             int h) {
   const int lane = threadIdx.x & 63;
@@ -596,11 +598,11 @@ __device__ __forceinline__ void mfma_stream(MfmaState<D, NRTW>& S, const Partial
   for (int kt = 0; kt < ntiles; kt += 2, base += 64) {
     load_tile_kv<D, FA>(bB, sgB, kb, vb, j, i, a);
     load_tile_seg(sgA, st, base + 64, last, i, j);
-    mfma_tile<D, NRTW, FAST>(S, bA, a, it, base, j);
+    mfma_tile<D, NRTW, HILO>(S, bA, a, it, base, j);
     if (kt + 1 >= ntiles) break;
     load_tile_kv<D, FA>(bA, sgA, kb, vb, j, i, a);
     load_tile_seg(sgB, st, base + 96, last, i, j);
-    mfma_tile<D, NRTW, FAST>(S, bB, a, it, base + 32, j);
+    mfma_tile<D, NRTW, HILO>(S, bB, a, it, base + 32, j);
   }
 }
 
@@ -634,48 +636,190 @@ __device__ __forceinline__ void mfma_write(MfmaState<D, NRTW>& S, const PartialA
   }
 }
 
-template <int D, int NRTW, bool FA, bool FAST>
+template <int D, int NRTW, bool FA>
 __device__ __forceinline__ void mfma_wave(const PartialArgs& a, const WorkItem& it, int h, const int (&rt)[NRTW],
                                           const bool (&on)[NRTW]) {
   MfmaState<D, NRTW> S;
   mfma_init(S, a, it, h, rt, on);
-  mfma_stream<D, NRTW, FA, FAST>(S, a, it, h);
+  if (it.flags & 1) mfma_stream<D, NRTW, FA, true>(S, a, it, h);
+  else mfma_stream<D, NRTW, FA, false>(S, a, it, h);
   mfma_write(S, a);
 }
 
 // ---------------------------------------------------------------------------
-// Workgroup items (groups with many rows): one workgroup per item x kv-head;
-// wave w owns row tiles w, w+4 (bf16) or row pairs (fp32).
+// Workgroup items, bf16: one workgroup per item x kv-head, K/V tiles shared
+// through LDS. Each 32-token tile is loaded once by the whole workgroup (every
+// thread one token-row slice of 64 bytes) into one of two LDS stages; the next
+// tile is in flight in registers while the current one is computed, and one
+// barrier per tile hands the stage over. Token rows are stored with their
+// 16-byte chunks XOR-swizzled by the token index, so the stores and the MFMA
+// operand reads (16 lanes = 16 tokens or 16 chunks) hit distinct banks.
+template <int D>
+struct LdsTile {
+  static constexpr int CH = D / 8;         // 16-byte chunks per token row
+  static constexpr int ROW = D * 2;        // bytes per token row
+  static constexpr int PART = 32 * ROW;    // one K or V tile
+  static constexpr int STAGE = 2 * PART;   // K then V
+  static __device__ __forceinline__ int off(int part, int t, int c) {
+    return part * PART + t * ROW + ((c ^ (t & (CH - 1))) << 4);
+  }
+};
+
+// thread -> (part = K or V, token 0..31, first chunk): 128 threads per part
+template <int D, bool FA>
+struct TileLoader {
+  static constexpr int NC = D / 32;  // 16-byte chunks per thread
+  typedef typename TokOff<FA>::type Off;
+  u32x4 r[NC];
+  int part, tok, c0;
+  const char* base;
+  __device__ __forceinline__ void init(const PartialArgs& a, int h) {
+    part = threadIdx.x >> 7;
+    const int idx = threadIdx.x & 127;
+    tok = idx & 31;
+    c0 = (idx >> 5) * NC;
+    base = pool_head(part ? a.v : a.k, a, h, 2);
+  }
+  __device__ __forceinline__ void load(int32_t sg, const PartialArgs& a) {
+    const Off off = TokOff<FA>::of(sg, a) + Off(c0 * 16);
+#pragma unroll
+    for (int x = 0; x < NC; ++x) r[x] = load_at<u32x4>(base, off + Off(16 * x));
+  }
+  __device__ __forceinline__ void store(char* stage) const {
+#pragma unroll
+    for (int x = 0; x < NC; ++x) *reinterpret_cast<u32x4*>(stage + LdsTile<D>::off(part, tok, c0 + x)) = r[x];
+  }
+};
+
+// One tile for the wave's first NACT row tiles, operands read straight from
+// an LDS stage: K one k-step at a time (the A operand of S^T for both token
+// blocks), then the eight V token slices (16 lanes of a row group read one
+// token's 16 chunks: distinct banks) and V^T two d-blocks at a time.
+template <int D, int NRTW, int NACT, bool HILO>
+__device__ __forceinline__ void lds_tile(MfmaState<D, NRTW>& S, const char* stage, const PartialArgs& a,
+                                         const WorkItem& it, int base, int i, int j) {
+  typedef LdsTile<D> L;
+  constexpr int KK = D / 32, DPL = D / 16;
+  f32x4 s0[NACT], s1[NACT];
+#pragma unroll
+  for (int k = 0; k < NACT; ++k) s0[k] = s1[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(stage + L::off(0, i, kk * 4 + j));
+    const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(stage + L::off(0, 16 + i, kk * 4 + j));
+#pragma unroll
+    for (int k = 0; k < NACT; ++k) {
+      s0[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, S.qf[k][kk], s0[k], 0, 0, 0);
+      s1[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, S.qf[k][kk], s1[k], 0, 0, 0);
+    }
+  }
+  bf16x8 pb[NACT], pl[NACT];
+#pragma unroll
+  for (int k = 0; k < NACT; ++k) mfma_softmax<D, NRTW, HILO>(S, k, s0[k], s1[k], a, it, base, j, pb[k], pl[k]);
+  VSlice<DPL> vs[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int t = tau(j, e);
+    if constexpr (D == 128) {
+      vs[e].w = *reinterpret_cast<const u32x4*>(stage + L::off(1, t, i));
+    } else {
+      vs[e].w = *reinterpret_cast<const u32x2*>(stage + L::off(1, t, i >> 1) + (i & 1) * 8);
+    }
+  }
+  // word w of a token's V slice holds d-blocks 2w (low halves) and 2w + 1
+#pragma unroll
+  for (int w = 0; w < DPL / 2; ++w) {
+    u32x4 lo, hi;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      lo[u] = __builtin_amdgcn_perm(vs[2 * u + 1].word(w), vs[2 * u].word(w), 0x05040100u);
+      hi[u] = __builtin_amdgcn_perm(vs[2 * u + 1].word(w), vs[2 * u].word(w), 0x07060302u);
+    }
+    const bf16x8 vlo = __builtin_bit_cast(bf16x8, lo), vhi = __builtin_bit_cast(bf16x8, hi);
+#pragma unroll
+    for (int k = 0; k < NACT; ++k) {
+      pv_update<D, NRTW, HILO>(S, k, 2 * w, vlo, pb[k], pl[k]);
+      pv_update<D, NRTW, HILO>(S, k, 2 * w + 1, vhi, pb[k], pl[k]);
+    }
+  }
+}
+
+// The tile loop of a workgroup item: two LDS stages, the next tile in
+// flight in registers while the current one is computed, one barrier per
+// tile. NACT (row tiles this wave computes) and HILO are fixed per loop.
+template <int D, bool FA, int NACT, bool HILO>
+__device__ __forceinline__ void lds_stream(MfmaState<D, kBlockRowTiles>& S, char* lds, const PartialArgs& a,
+                                           const WorkItem& it, int h, int i, int j) {
+  const int ntiles = (it.tok1 - it.tok0 + 31) >> 5;
+  const int32_t* st = a.seg_tok + it.seg_base;
+  const int last = it.tok1 - 1;
+  TileLoader<D, FA> ld;
+  ld.init(a, h);
+  ld.load(st[min(it.tok0 + ld.tok, last)], a);
+  int32_t sg_next = st[min(it.tok0 + 32 + ld.tok, last)];
+  ld.store(lds);
+  __syncthreads();
+  for (int n = 0; n < ntiles; ++n) {
+    const bool more = n + 1 < ntiles;
+    if (more) {
+      ld.load(sg_next, a);
+      sg_next = st[min(it.tok0 + (n + 2) * 32 + ld.tok, last)];
+    }
+    if constexpr (NACT > 0)
+      lds_tile<D, kBlockRowTiles, NACT, HILO>(S, lds + (n & 1) * LdsTile<D>::STAGE, a, it, it.tok0 + n * 32, i, j);
+    if (more) ld.store(lds + ((n + 1) & 1) * LdsTile<D>::STAGE);
+    __syncthreads();
+  }
+}
+
+template <int D, bool FA>
+__global__ __launch_bounds__(kBlock, 2) void block_lds_kernel(PartialArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[2 * LdsTile<D>::STAGE];
+  const int item = blockIdx.x / a.n_kvheads;
+  const int h = blockIdx.x - item * a.n_kvheads;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 15, j = lane >> 4;
+  const WorkItem it = a.items[item];
+  const int nrt = (it.nrows + 15) >> 4;
+  const bool hilo = it.flags & 1;
+  // row tiles beyond kWaves * kBlockRowTiles take further passes over the
+  // chunk (the planner's row blocks keep this to one pass)
+  for (int r0 = 0; r0 < nrt; r0 += kWaves * kBlockRowTiles) {
+    int rt[kBlockRowTiles];
+    bool on[kBlockRowTiles];
+#pragma unroll
+    for (int k = 0; k < kBlockRowTiles; ++k) {
+      rt[k] = r0 + wave + kWaves * k;
+      on[k] = rt[k] < nrt;
+    }
+    MfmaState<D, kBlockRowTiles> S;
+    mfma_init(S, a, it, h, rt, on);
+    // every wave takes part in the loads and barriers, computing or not
+    if (S.on[1]) {
+      if (hilo) lds_stream<D, FA, 2, true>(S, lds, a, it, h, i, j);
+      else lds_stream<D, FA, 2, false>(S, lds, a, it, h, i, j);
+    } else if (S.on[0]) {
+      if (hilo) lds_stream<D, FA, 1, true>(S, lds, a, it, h, i, j);
+      else lds_stream<D, FA, 1, false>(S, lds, a, it, h, i, j);
+    } else {
+      lds_stream<D, FA, 0, false>(S, lds, a, it, h, i, j);
+    }
+    mfma_write(S, a);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Workgroup items, fp32 (GEMV path): one workgroup per item x kv-head; wave
+// w owns row pairs 2w, 2w + 8, ... over the whole chunk.
 template <typename T, int D, bool FA>
 __global__ __launch_bounds__(kBlock) void block_items_kernel(PartialArgs a) {
+  static_assert(std::is_same<T, float>::value, "bf16 workgroup items use block_lds_kernel");
   const int item = blockIdx.x / a.n_kvheads;
   const int h = blockIdx.x - item * a.n_kvheads;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const WorkItem it = a.items[item];
-  if constexpr (std::is_same<T, __bf16>::value) {
-    const int nrt = (it.nrows + 15) >> 4;
-    if (wave >= nrt) return;
-    if (nrt <= 4) {
-      const int rt1[1] = {wave};
-      const bool on1[1] = {true};
-      mfma_wave<D, 1, FA, true>(a, it, h, rt1, on1);
-    } else {
-      // up to kBlockRowTiles row tiles per wave; rows beyond them take
-      // further passes (the planner's row blocks keep this to one pass)
-      for (int r0 = 0; r0 < nrt; r0 += kWaves * kBlockRowTiles) {
-        int rt[kBlockRowTiles];
-        bool on[kBlockRowTiles];
-#pragma unroll
-        for (int k = 0; k < kBlockRowTiles; ++k) {
-          rt[k] = r0 + wave + kWaves * k;
-          on[k] = rt[k] < nrt;
-        }
-        if (on[0]) mfma_wave<D, kBlockRowTiles, FA, true>(a, it, h, rt, on);
-      }
-    }
-  } else {
-    for (int r = 2 * wave; r < it.nrows; r += 2 * kWaves) valu_wave_item<T, D, 2, FA>(a, it, h, r);
-  }
+  for (int r = 2 * wave; r < it.nrows; r += 2 * kWaves) valu_wave_item<T, D, 2, FA>(a, it, h, r);
 }
 
 // Single-wave items (groups with few rows): each wave of the launch is one
@@ -692,7 +836,7 @@ __global__ __launch_bounds__(kBlock, 2) void wave_items_kernel(PartialArgs a, in
     if (it.nrows > kValuMaxRows) {
       const int rt[1] = {0};
       const bool on[1] = {true};
-      mfma_wave<D, 1, FA, false>(a, it, h, rt, on);
+      mfma_wave<D, 1, FA>(a, it, h, rt, on);
       return;
     }
   }
@@ -704,51 +848,84 @@ __global__ __launch_bounds__(kBlock, 2) void wave_items_kernel(PartialArgs a, in
 }
 
 // ---------------------------------------------------------------------------
-// One wave handles 64 / (D / 4) (query, q-head) pairs, D / 4 lanes each with
-// a float4 of the output. Slots are read in batches of 8 so their loads are in
-// flight together; each batch is folded into the running (M, L, acc).
-constexpr int kReduceBatch = 8;
+// One wave per (query, q-head). The wave's four 16-lane groups take every
+// fourth of the query's slots (each lane D/16 consecutive output elements),
+// loading them in batches of 4 so the loads are in flight together; the
+// groups' (M, L, acc) are then merged with two permlane swaps and group 0
+// writes the normalised output.
+constexpr int kReduceBatch = 4;
+constexpr int kReduceGroups = 4;
 
 template <int D>
-__global__ __launch_bounds__(64) void lse_reduce_kernel(ReduceArgs a) {
-  constexpr int LP = D / 4;
-  constexpr int PPW = 64 / LP;
-  const int pair = blockIdx.x * PPW + threadIdx.x / LP;
-  const int sub = threadIdx.x % LP;
+__global__ __launch_bounds__(kBlock) void lse_reduce_kernel(ReduceArgs a) {
+  constexpr int EPL = D / 16;      // output elements per lane
+  const int pair = blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (pair >= a.n_queries * a.n_qheads) return;
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, sub = lane & 15;
   const int q = pair / a.n_qheads;
   const int hq = pair - q * a.n_qheads;
   float M = TA_NEG_INF, L = 0.0f;
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  float acc[EPL];
+#pragma unroll
+  for (int x = 0; x < EPL; ++x) acc[x] = 0.0f;
   const int s0 = a.q_slot_ptr[q], s1 = a.q_slot_ptr[q + 1];
-  for (int b = s0; b < s1; b += kReduceBatch) {
+  for (int b = s0 + g; b < s1; b += kReduceGroups * kReduceBatch) {
     int64_t pi[kReduceBatch];
 #pragma unroll
-    for (int u = 0; u < kReduceBatch; ++u) pi[u] = int64_t(a.q_slots[min(b + u, s1 - 1)]) * a.n_qheads + hq;
+    for (int u = 0; u < kReduceBatch; ++u)
+      pi[u] = int64_t(a.q_slots[min(b + kReduceGroups * u, s1 - 1)]) * a.n_qheads + hq;
     float mv[kReduceBatch], lv[kReduceBatch];
-    f32x4 ov[kReduceBatch];
+    f32x4 ov[kReduceBatch][EPL / 4];
 #pragma unroll
     for (int u = 0; u < kReduceBatch; ++u) {
-      mv[u] = (b + u < s1) ? a.m_part[pi[u]] : TA_NEG_INF;
+      mv[u] = (b + kReduceGroups * u < s1) ? a.m_part[pi[u]] : TA_NEG_INF;
       lv[u] = a.l_part[pi[u]];
-      ov[u] = *reinterpret_cast<const f32x4*>(a.o_part + pi[u] * D + sub * 4);
+#pragma unroll
+      for (int c = 0; c < EPL / 4; ++c)
+        ov[u][c] = *reinterpret_cast<const f32x4*>(a.o_part + pi[u] * D + sub * EPL + 4 * c);
     }
     float Mn = M;
 #pragma unroll
     for (int u = 0; u < kReduceBatch; ++u) Mn = fmaxf(Mn, mv[u]);
     const float wa = part_weight(M, Mn);
-    acc *= wa;
     L *= wa;
+#pragma unroll
+    for (int x = 0; x < EPL; ++x) acc[x] *= wa;
 #pragma unroll
     for (int u = 0; u < kReduceBatch; ++u) {
       const float w = part_weight(mv[u], Mn);
-      acc += ov[u] * w;
       L += lv[u] * w;
+#pragma unroll
+      for (int c = 0; c < EPL / 4; ++c)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) acc[4 * c + y] += ov[u][c][y] * w;
     }
     M = Mn;
   }
-  const float inv = 1.0f / L;
-  *reinterpret_cast<f32x4*>(a.out + (int64_t(q) * a.n_qheads + hq) * D + sub * 4) = acc * inv;
+  // merge the four slot groups (lanes sub, sub+16, sub+32, sub+48)
+#pragma unroll
+  for (int step = 0; step < 2; ++step) {
+    const float Mo = step == 0 ? xor16(M) : xor32(M);
+    const float Lo = step == 0 ? xor16(L) : xor32(L);
+    const float Mn = fmaxf(M, Mo);
+    const float ws = part_weight(M, Mn), wo = part_weight(Mo, Mn);
+    L = L * ws + Lo * wo;
+#pragma unroll
+    for (int x = 0; x < EPL; ++x) {
+      const float ao = step == 0 ? xor16(acc[x]) : xor32(acc[x]);
+      acc[x] = acc[x] * ws + ao * wo;
+    }
+    M = Mn;
+  }
+  if (g == 0) {
+    const float inv = 1.0f / L;
+    float* op = a.out + (int64_t(q) * a.n_qheads + hq) * D + sub * EPL;
+#pragma unroll
+    for (int c = 0; c < EPL / 4; ++c)
+      *reinterpret_cast<f32x4*>(op + 4 * c) =
+          f32x4{acc[4 * c] * inv, acc[4 * c + 1] * inv, acc[4 * c + 2] * inv, acc[4 * c + 3] * inv};
+  }
 }
 
 __global__ void fill_kernel(float* p, int64_t n, float value) {
@@ -759,8 +936,13 @@ __global__ void fill_kernel(float* p, int64_t n, float value) {
 template <typename T, int D>
 void launch_block_t(const PartialArgs& a, int32_t n_block_items, hipStream_t s) {
   const dim3 grid(unsigned(n_block_items) * a.n_kvheads), block(kBlock);
-  if (a.fast_addr) hipLaunchKernelGGL((block_items_kernel<T, D, true>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((block_items_kernel<T, D, false>), grid, block, 0, s, a);
+  if constexpr (std::is_same<T, __bf16>::value) {
+    if (a.fast_addr) hipLaunchKernelGGL((block_lds_kernel<D, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((block_lds_kernel<D, false>), grid, block, 0, s, a);
+  } else {
+    if (a.fast_addr) hipLaunchKernelGGL((block_items_kernel<T, D, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((block_items_kernel<T, D, false>), grid, block, 0, s, a);
+  }
 }
 
 template <typename T, int D>
@@ -802,8 +984,7 @@ hipError_t launch_wave_items(const PartialArgs& a, int32_t item0, int32_t n_wave
 hipError_t launch_reduce(const ReduceArgs& a, int head_dim, hipStream_t s) {
   const int64_t pairs = int64_t(a.n_queries) * a.n_qheads;
   if (pairs <= 0) return hipSuccess;
-  const int ppw = 64 / (head_dim / 4);
-  const dim3 grid(unsigned((pairs + ppw - 1) / ppw)), block(64);
+  const dim3 grid(unsigned((pairs + kWaves - 1) / kWaves)), block(kBlock);
   if (head_dim == 128) hipLaunchKernelGGL(lse_reduce_kernel<128>, grid, block, 0, s, a);
   else hipLaunchKernelGGL(lse_reduce_kernel<64>, grid, block, 0, s, a);
   return hipGetLastError();
