@@ -115,7 +115,8 @@ def main():
     wall = time.perf_counter() - t0
     ref_out = out.clone()
 
-    # per-kernel device time (HIP events recorded by the library on the launch stream)
+    # per-kernel device time: the library launches each kernel with HIP
+    # start/stop events stamped at that kernel's own start and end
     plan.timing_enable(K)
     for s in range(K):
         calls[s % copies]()
@@ -159,6 +160,7 @@ def main():
     ms_per_step = wall * 1e3 / K
     part_us = float(np.mean(pm)) * 1e3
     red_us = float(np.mean(rm)) * 1e3
+    dominant = f"partial_kernel<{'bf16' if inst.dtype == torch.bfloat16 else 'f32'},{inst.head_dim}>"
     value = unique / (ms_per_step * 1e-3) / 1e9
     achieved = unique / (part_us * 1e-6) / 1e9
     res = {
@@ -196,7 +198,8 @@ def main():
                        "partial_attn_warm": round(float(np.mean(pm_w)) * 1e3, 3),
                        "lse_reduce_warm": round(float(np.mean(rm_w)) * 1e3, 3)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": dominant, "kernel_us": round(part_us, 3)},
         "graph_us_per_step": round(graph_us, 3) if isinstance(graph_us, float) else graph_us,
         "planner_host_ms": {"tables_median": round(statistics.median(t_host) * 1e3, 3),
                             "with_upload": round(t_plan_full * 1e3, 3)},

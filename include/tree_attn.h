@@ -124,12 +124,15 @@ ta_status tree_attn_plan_info(const ta_plan* plan, int32_t* n_queries, int64_t* 
 ta_status tree_attn_plan_export(const ta_plan* plan, int32_t table_id, int32_t* dst, int64_t* len);
 
 /* Timing of the last decodes (testing and benchmarking). After
- * tree_attn_timing_enable(plan, capacity) every decode records HIP events
- * around its two kernels on its stream, for up to `capacity` decodes
- * (capacity 0 turns timing off). tree_attn_timing_read() waits for the
- * recorded events and writes per-decode milliseconds of the partial-attention
- * kernel and of the reduction kernel; *n gets the count and the record is
- * cleared. */
+ * tree_attn_timing_enable(plan, capacity) every decode, for up to `capacity`
+ * decodes, launches its two kernels with HIP start/stop events that the
+ * runtime stamps at the start and at the end of each kernel's own execution
+ * (not at enqueue); capacity 0 turns timing off. Do not enable timing on a
+ * decode that is being captured into a graph.
+ * tree_attn_timing_read() waits for the recorded events and writes per-decode
+ * milliseconds of the partial-attention kernel (partial_ms[x]) and of the
+ * reduction kernel (reduce_ms[x]); either pointer may be NULL. *n gets the
+ * count and the record is cleared. */
 ta_status tree_attn_timing_enable(ta_plan* plan, int32_t capacity);
 ta_status tree_attn_timing_read(ta_plan* plan, float* partial_ms, float* reduce_ms, int32_t* n);
 

@@ -169,23 +169,28 @@ def test_decode_argument_errors():
     plan.close()
 
 
-def test_timing_records():
-    inst = synth.make_config(2)
-    q, k, v = _dev(inst)
+@pytest.mark.parametrize("k", [2, 5])
+def test_timing_records(k):
+    """Per-kernel timing records, on a plan with one item class (config 2)
+    and one with both (config 5)."""
+    inst = synth.make_config(k)
+    q, k_, v = _dev(inst)
     plan = Plan.for_instance(inst)
     plan.timing_enable(4)
     for _ in range(3):
-        plan.decode(q, k, v)
+        plan.decode(q, k_, v)
     pm, rm = plan.timing_read(4)
     assert len(pm) == 3 and (pm > 0).all() and (rm > 0).all()
+    assert len(plan.timing_read(4)[0]) == 0          # the read cleared the record
+    plan.decode(q, k_, v)
+    assert len(plan.timing_read(4)[0]) == 1
     plan.close()
 
 
 def test_graph_capture_replays():
-    """A decode captured in a HIP graph (through torch's graph capture; the
-    plan forks its workgroup items onto a side stream and joins back) replays
-    to the eager result, with eager decodes and synchronisations between the
-    replays."""
+    """A decode captured in a HIP graph (through torch's graph capture, on a
+    plan with both item classes) replays to the eager result, with eager
+    decodes and synchronisations between the replays."""
     inst = synth.make_config(5)
     q, k, v = _dev(inst)
     plan = Plan.for_instance(inst)

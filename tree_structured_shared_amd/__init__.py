@@ -146,6 +146,8 @@ class Plan:
         check(lib().tree_attn_timing_enable(self._handle, int(capacity)))
 
     def timing_read(self, capacity):
+        """Per-decode kernel milliseconds (partial, reduce), each kernel timed
+        from its own start to its own end."""
         pm = (ctypes.c_float * max(1, capacity))()
         rm = (ctypes.c_float * max(1, capacity))()
         n = ctypes.c_int32()

@@ -43,11 +43,8 @@ struct ta_plan {
   void* d_ws = nullptr;  // workspace: o_part | m_part | l_part
   float *d_o_part = nullptr, *d_m_part = nullptr, *d_l_part = nullptr;
   int64_t ws_bytes = 0;
-  std::vector<hipEvent_t> ev;  // 3 per timed decode
-  // side stream: workgroup items run there while single-wave items run on
-  // the caller's stream (fork and join through two events, default priority)
-  hipStream_t side = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
+  // 4 per timed decode: start/stop of the partial kernel and of the reduction
+  std::vector<hipEvent_t> ev;
   int32_t timing_cap = 0, timing_n = 0;
 };
 
@@ -78,11 +75,6 @@ void free_device(ta_plan* p) {
   if (p->host_only) return;
   for (hipEvent_t e : p->ev) (void)hipEventDestroy(e);
   p->ev.clear();
-  if (p->fork) (void)hipEventDestroy(p->fork);
-  if (p->join) (void)hipEventDestroy(p->join);
-  if (p->side) (void)hipStreamDestroy(p->side);
-  p->fork = p->join = nullptr;
-  p->side = nullptr;
   if (p->d_tables) (void)hipFree(p->d_tables);
   if (p->d_ws) (void)hipFree(p->d_ws);
   p->d_tables = p->d_ws = nullptr;
@@ -155,12 +147,6 @@ ta_status upload(ta_plan* p) {
   if (e != hipSuccess) {
     p->d_ws = nullptr;
     return set_err(TA_ENOMEM, std::string("tree_attn_plan: hipMalloc(workspace): ") + hipGetErrorString(e));
-  }
-  if (T.n_stream_items > 0 && T.n_stream_items < T.n_items) {
-    if ((e = hipStreamCreateWithFlags(&p->side, hipStreamNonBlocking)) != hipSuccess ||
-        (e = hipEventCreateWithFlags(&p->fork, hipEventDisableTiming)) != hipSuccess ||
-        (e = hipEventCreateWithFlags(&p->join, hipEventDisableTiming)) != hipSuccess)
-      return hip_err(e, "tree_attn_plan: side stream");
   }
   uint8_t* wb = static_cast<uint8_t*>(p->d_ws);
   p->d_o_part = reinterpret_cast<float*>(wb);
@@ -285,8 +271,12 @@ ta_status tree_attn_decode(const void* q, ta_dtype q_dtype, const ta_paged_kv* k
     e = ta::launch_fill(mp->d_o_part, mp->ws_bytes / 4, std::nanf(""), s);
     if (e != hipSuccess) return hip_err(e, "tree_attn_decode: poison fill");
   }
-  if (timed && (e = hipEventRecord(mp->ev[3 * mp->timing_n], s)) != hipSuccess)
-    return hip_err(e, "tree_attn_decode: hipEventRecord");
+  ta::KernelTimer t_part, t_red;
+  if (timed) {
+    hipEvent_t* ev = &mp->ev[4 * size_t(mp->timing_n)];
+    t_part = {ev[0], ev[1]};
+    t_red = {ev[2], ev[3]};
+  }
 
   ta::PartialArgs a{};
   a.items = plan->d_items;
@@ -316,23 +306,8 @@ ta_status tree_attn_decode(const void* q, ta_dtype q_dtype, const ta_paged_kv* k
   a.scale_log2 = plan->scale * 1.4426950408889634f;
   const int dt = q_dtype == TA_BF16 ? 1 : 0;
   const int32_t n_block = plan->T.n_items - plan->T.n_stream_items, n_wave = plan->T.n_stream_items;
-  if (n_block > 0 && n_wave > 0) {
-    if ((e = hipEventRecord(plan->fork, s)) != hipSuccess || (e = hipStreamWaitEvent(plan->side, plan->fork, 0)) != hipSuccess)
-      return hip_err(e, "tree_attn_decode: fork");
-    if ((e = ta::launch_block_items(a, n_block, dt, plan->head_dim, plan->side)) != hipSuccess)
-      return hip_err(e, "tree_attn_decode: workgroup-item launch");
-    if ((e = ta::launch_wave_items(a, n_block, n_wave, dt, plan->head_dim, s)) != hipSuccess)
-      return hip_err(e, "tree_attn_decode: single-wave-item launch");
-    if ((e = hipEventRecord(plan->join, plan->side)) != hipSuccess || (e = hipStreamWaitEvent(s, plan->join, 0)) != hipSuccess)
-      return hip_err(e, "tree_attn_decode: join");
-  } else {
-    if ((e = ta::launch_block_items(a, n_block, dt, plan->head_dim, s)) != hipSuccess)
-      return hip_err(e, "tree_attn_decode: workgroup-item launch");
-    if ((e = ta::launch_wave_items(a, n_block, n_wave, dt, plan->head_dim, s)) != hipSuccess)
-      return hip_err(e, "tree_attn_decode: single-wave-item launch");
-  }
-  if (timed && (e = hipEventRecord(mp->ev[3 * mp->timing_n + 1], s)) != hipSuccess)
-    return hip_err(e, "tree_attn_decode: hipEventRecord");
+  if ((e = ta::launch_partial(a, n_block, n_wave, dt, plan->head_dim, s, t_part)) != hipSuccess)
+    return hip_err(e, "tree_attn_decode: partial-attention launch");
 
   ta::ReduceArgs r{};
   r.q_slot_ptr = plan->d_q_slot_ptr;
@@ -343,13 +318,9 @@ ta_status tree_attn_decode(const void* q, ta_dtype q_dtype, const ta_paged_kv* k
   r.out = out;
   r.n_queries = plan->T.n_queries;
   r.n_qheads = plan->n_qheads;
-  e = ta::launch_reduce(r, plan->head_dim, s);
+  e = ta::launch_reduce(r, plan->head_dim, s, t_red);
   if (e != hipSuccess) return hip_err(e, "tree_attn_decode: reduction launch");
-  if (timed) {
-    if ((e = hipEventRecord(mp->ev[3 * mp->timing_n + 2], s)) != hipSuccess)
-      return hip_err(e, "tree_attn_decode: hipEventRecord");
-    ++mp->timing_n;
-  }
+  if (timed) ++mp->timing_n;
   return TA_OK;
 }
 
@@ -393,7 +364,7 @@ ta_status tree_attn_timing_enable(ta_plan* plan, int32_t capacity) {
   plan->timing_cap = 0;
   plan->timing_n = 0;
   try {
-    plan->ev.resize(size_t(capacity) * 3);
+    plan->ev.resize(size_t(capacity) * 4);
   } catch (const std::bad_alloc&) {
     return set_err(TA_ENOMEM, "tree_attn_timing_enable: host allocation failed");
   }
@@ -413,12 +384,13 @@ ta_status tree_attn_timing_read(ta_plan* plan, float* partial_ms, float* reduce_
   if (!plan || !n) return set_err(TA_EINVAL, "tree_attn_timing_read: NULL argument");
   const int32_t cnt = plan->timing_n;
   for (int32_t x = 0; x < cnt; ++x) {
-    hipError_t e = hipEventSynchronize(plan->ev[3 * x + 2]);
+    const hipEvent_t* ev = &plan->ev[4 * size_t(x)];
+    hipError_t e = hipEventSynchronize(ev[3]);
+    if (e == hipSuccess) e = hipEventSynchronize(ev[1]);
     if (e != hipSuccess) return hip_err(e, "tree_attn_timing_read: hipEventSynchronize");
     float t0 = 0.0f, t1 = 0.0f;
-    if ((e = hipEventElapsedTime(&t0, plan->ev[3 * x], plan->ev[3 * x + 1])) != hipSuccess)
-      return hip_err(e, "tree_attn_timing_read: hipEventElapsedTime");
-    if ((e = hipEventElapsedTime(&t1, plan->ev[3 * x + 1], plan->ev[3 * x + 2])) != hipSuccess)
+    if ((e = hipEventElapsedTime(&t0, ev[0], ev[1])) != hipSuccess ||
+        (e = hipEventElapsedTime(&t1, ev[2], ev[3])) != hipSuccess)
       return hip_err(e, "tree_attn_timing_read: hipEventElapsedTime");
     if (partial_ms) partial_ms[x] = t0;
     if (reduce_ms) reduce_ms[x] = t1;

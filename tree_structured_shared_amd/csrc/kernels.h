@@ -55,15 +55,19 @@ struct ReduceArgs {
   int32_t n_queries, n_qheads;
 };
 
-// dtype: 0 = fp32, 1 = bf16 (Q, K and V share it).
-// Items [0, n_block_items) run one workgroup per item x kv-head; items
-// [item0, item0 + n_wave_items) run one wave per item x kv-head. The two
-// launches touch disjoint partial slots and may run concurrently.
-hipError_t launch_block_items(const PartialArgs& a, int32_t n_block_items, int dtype, int head_dim,
-                              hipStream_t s);
-hipError_t launch_wave_items(const PartialArgs& a, int32_t item0, int32_t n_wave_items, int dtype,
-                             int head_dim, hipStream_t s);
-hipError_t launch_reduce(const ReduceArgs& a, int head_dim, hipStream_t s);
+// Each launcher takes an optional pair of timing events (both null or both
+// created with timing): they are stamped with the start and the end of that
+// kernel's own execution (hipExtLaunchKernelGGL), not of the enqueue.
+struct KernelTimer {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+// dtype: 0 = fp32, 1 = bf16 (Q, K and V share it). Items [0, n_block_items)
+// are workgroup items (one workgroup per item x kv-head), the next
+// n_wave_items single-wave items (one wave per item x kv-head); one launch.
+hipError_t launch_partial(const PartialArgs& a, int32_t n_block_items, int32_t n_wave_items, int dtype,
+                          int head_dim, hipStream_t s, KernelTimer t = {});
+hipError_t launch_reduce(const ReduceArgs& a, int head_dim, hipStream_t s, KernelTimer t = {});
 hipError_t launch_fill(float* p, int64_t n, float value, hipStream_t s);
 
 }  // namespace ta

@@ -9,23 +9,25 @@
 // notes, attention calculation; FastTree review, tile-by-tile online softmax).
 // Each row ends in one unnormalised partial (m, l, o) in the workspace.
 //
-//  * wave_items_kernel: groups with few rows. Each wave of the launch is one
-//    item x kv-head.
-//  * block_lds_kernel: groups with many rows (bf16). One workgroup per item
-//    x kv-head; the workgroup loads each K/V tile once into LDS (two stages,
-//    one barrier per tile) and wave w computes row tiles w and w+4 (128 rows
-//    per workgroup) from it. fp32 workgroup items (block_items_kernel) run
-//    the GEMV path per wave.
-// Two row paths, chosen per item by its row count (the review's multi-stage
-// query tiling: small tiles near the leaves, large ones near the root):
-//  * GEMV-sized items (one or two rows, and every fp32 item): wavefront dot
-//    products, 8 lanes per token, DPP reductions, per-lane online softmax.
-//  * GEMM-sized bf16 items: v_mfma_f32_16x16x32_bf16 on a transposed
-//    formulation. S^T = K Q^T: K rows are the A operand, loaded straight from
-//    the pool. O^T = V^T P^T: the score accumulators already sit in the
-//    B-operand layout of P^T, and V^T comes from a v_perm transpose of 16-byte
-//    V loads (stacking the queries that share KV turns the decode GEMV into a
-//    GEMM, FastTree review, kernel design).
+// One launch (partial_kernel) holds both item classes, chosen per group by
+// its row count (the review's multi-stage query tiling: small tiles near the
+// leaves, large ones near the root):
+//  * workgroup items (many rows): one workgroup per item x kv-head. bf16:
+//    the workgroup loads each K/V tile once into LDS (two stages, one
+//    barrier per tile) and wave w computes row tiles w and w+4 (128 rows per
+//    workgroup) from it. fp32: each wave runs the GEMV path on row pairs.
+//  * single-wave items (up to 16 rows): each wave is one item x kv-head and
+//    streams its chunk alone with two tiles in flight.
+// Row arithmetic:
+//  * bf16: v_mfma_f32_16x16x32_bf16 on a transposed formulation, 16-row
+//    tiles (padded for fewer rows: the items are bound by their K/V stream).
+//    S^T = K Q^T: K rows are the A operand, loaded straight from the pool.
+//    O^T = V^T P^T: the score accumulators already sit in the B-operand
+//    layout of P^T, and V^T comes from a v_perm transpose of 16-byte V loads
+//    (stacking the queries that share KV turns the decode GEMV into a GEMM,
+//    FastTree review, kernel design).
+//  * fp32: wavefront dot products (GEMV), 8 lanes per token, DPP reductions,
+//    per-lane online softmax.
 //
 // lse_reduce: per (query, q-head), merges that query's partials along its
 // path (root-side group first, chunks ascending) by log-sum-exp -- the
@@ -36,6 +38,8 @@
 // score exceeds it by more than 8 (log2 units), so rescaling is rare; l and o
 // always stay relative to the stored m.
 #include "kernels.h"
+
+#include <hip/hip_ext.h>
 
 #include <type_traits>
 
@@ -49,7 +53,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBlock = 256;
 constexpr int kWaves = 4;
-constexpr int kValuMaxRows = 2;   // bf16 items with more rows take the MFMA path
 constexpr int kBlockRowTiles = 2; // 16-row tiles per wave in workgroup items
 constexpr float kRescale = 8.0f;  // lazy-rescale threshold, log2 units
 // initial running max of the MFMA path: finite, so exp2(s - m) of a masked
@@ -264,9 +267,10 @@ __device__ __forceinline__ void valu_step(ValuState<T, D, R>& S, const Slice<T, 
 }
 
 // Steps of 16 tokens over [wb, we). Two buffers alternate with no register
-// copies, so the wait before each step's arithmetic covers only older loads:
-// page-table entries run one step ahead of K/V, K/V one step ahead of the
-// math. Loads past the end clamp to the last token (cache-resident, unused).
+// copies. Each step's page-table entries are requested before the K/V of the
+// step ahead of it (loads retire in issue order for the wait counter), so
+// two steps of K/V stay in flight while one is computed. Loads past the end
+// clamp to the last token (cache-resident, unused).
 template <typename T, int D, int R, bool FA>
 __device__ __forceinline__ void valu_stream(ValuState<T, D, R>& S, const PartialArgs& a,
                                             const WorkItem& it, int h, int wb, int we) {
@@ -295,16 +299,20 @@ __device__ __forceinline__ void valu_stream(ValuState<T, D, R>& S, const Partial
     }
   };
   seg(sA, wb);
-  kv(kA, vA, sA);
   seg(sB, wb + 16);
+  kv(kA, vA, sA);
+  seg(sA, wb + 32);
+  kv(kB, vB, sB);
+  seg(sB, wb + 48);
+  // no exit inside the body (it would make the compiler drain every load
+  // at the back edge): the second half is skipped wave-uniformly at the end
   for (int base = wb; base < we; base += 32) {
-    kv(kB, vB, sB);
-    seg(sA, base + 32);
     valu_step(S, kA, vA, a, base, we, tg);
-    if (base + 16 >= we) break;
     kv(kA, vA, sA);
-    seg(sB, base + 48);
-    valu_step(S, kB, vB, a, base + 16, we, tg);
+    seg(sA, base + 64);
+    if (base + 16 < we) valu_step(S, kB, vB, a, base + 16, we, tg);
+    kv(kB, vB, sB);
+    seg(sB, base + 80);
   }
 }
 
@@ -441,17 +449,19 @@ __device__ __forceinline__ void mfma_init(MfmaState<D, NRTW>& S, const PartialAr
   }
 }
 
-// page-table entries of one 32-token tile: the lane's two K tokens and its
-// eight V tokens (clamped to the chunk's last token past its end)
+// page-table entries of one 32-token tile: lane l holds token (l mod 32)'s
+// entry (clamped to the chunk's last token past its end); the K and V loads
+// fetch the entries they need from the owning lanes (ds_bpermute)
 struct TileSeg {
-  int32_t k[2], v[8];
+  int32_t mine;
 };
 
-__device__ __forceinline__ void load_tile_seg(TileSeg& t, const int32_t* st, int base, int last, int i, int j) {
-#pragma unroll
-  for (int tb = 0; tb < 2; ++tb) t.k[tb] = st[min(base + tb * 16 + i, last)];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) t.v[e] = st[min(base + tau(j, e), last)];
+__device__ __forceinline__ void load_tile_seg(TileSeg& t, const int32_t* st, int base, int last, int, int) {
+  t.mine = st[min(base + int(threadIdx.x & 31), last)];
+}
+
+__device__ __forceinline__ int32_t seg_of(const TileSeg& t, int tok) {
+  return __builtin_amdgcn_ds_bpermute(tok << 2, t.mine);
 }
 
 // one 32-token K/V tile in MFMA operand order
@@ -468,12 +478,12 @@ __device__ __forceinline__ void load_tile_kv(TileKV<D>& b, const TileSeg& sg, co
   constexpr int DPL = D / 16;
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb) {
-    const Off off = TokOff<FA>::of(sg.k[tb], a) + Off(j * 16);
+    const Off off = TokOff<FA>::of(seg_of(sg, tb * 16 + i), a) + Off(j * 16);
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) b.k[tb][kk] = load_at<u32x4>(kb, off + Off(kk * 64));
   }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) b.v[e].load(vb, TokOff<FA>::of(sg.v[e], a) + Off(i * DPL * 2));
+  for (int e = 0; e < 8; ++e) b.v[e].load(vb, TokOff<FA>::of(seg_of(sg, tau(j, e)), a) + Off(i * DPL * 2));
 }
 
 // softmax of one row tile's 32 scores: raises the running max when needed,
@@ -576,8 +586,10 @@ __device__ __forceinline__ void mfma_tile(MfmaState<D, NRTW>& S, const TileKV<D>
 }
 
 // Stream the item's 32-token tiles. Two tile buffers alternate with no
-// register copies (as in valu_stream): while tile n is computed, tile n + 1's
-// K/V and tile n + 2's page-table entries are in flight.
+// register copies. Memory loads complete in issue order as far as the wait
+// counter is concerned, so every tile's page-table entries are requested
+// before the K/V of the tile ahead of it: waiting for them then never waits
+// for younger K/V data, and two tiles stay in flight while one is computed.
 template <int D, int NRTW, bool FA, bool HILO>
 __device__ __forceinline__ void mfma_stream(MfmaState<D, NRTW>& S, const PartialArgs& a, const WorkItem& it,
                                             int h) {
@@ -589,20 +601,27 @@ __device__ __forceinline__ void mfma_stream(MfmaState<D, NRTW>& S, const Partial
   const int32_t* st = a.seg_tok + it.seg_base;
   const int last = it.tok1 - 1;
 
+  // issue order: seg 0, seg 1, kv 0, seg 2, kv 1, seg 3, then per tile n:
+  // compute n, kv n + 2, seg n + 4
   TileSeg sgA, sgB;
   TileKV<D> bA, bB;
   int base = it.tok0;
   load_tile_seg(sgA, st, base, last, i, j);
-  load_tile_kv<D, FA>(bA, sgA, kb, vb, j, i, a);
   load_tile_seg(sgB, st, base + 32, last, i, j);
+  load_tile_kv<D, FA>(bA, sgA, kb, vb, j, i, a);
+  load_tile_seg(sgA, st, base + 64, last, i, j);
+  load_tile_kv<D, FA>(bB, sgB, kb, vb, j, i, a);
+  load_tile_seg(sgB, st, base + 96, last, i, j);
+  // no exit inside the body (an exit between the two halves makes the
+  // compiler drain every load at the back edge): the second half is skipped
+  // wave-uniformly on an odd last tile
   for (int kt = 0; kt < ntiles; kt += 2, base += 64) {
-    load_tile_kv<D, FA>(bB, sgB, kb, vb, j, i, a);
-    load_tile_seg(sgA, st, base + 64, last, i, j);
     mfma_tile<D, NRTW, HILO>(S, bA, a, it, base, j);
-    if (kt + 1 >= ntiles) break;
     load_tile_kv<D, FA>(bA, sgA, kb, vb, j, i, a);
-    load_tile_seg(sgB, st, base + 96, last, i, j);
-    mfma_tile<D, NRTW, HILO>(S, bB, a, it, base + 32, j);
+    load_tile_seg(sgA, st, base + 128, last, i, j);
+    if (kt + 1 < ntiles) mfma_tile<D, NRTW, HILO>(S, bB, a, it, base + 32, j);
+    load_tile_kv<D, FA>(bB, sgB, kb, vb, j, i, a);
+    load_tile_seg(sgB, st, base + 160, last, i, j);
   }
 }
 
@@ -773,10 +792,9 @@ __device__ __forceinline__ void lds_stream(MfmaState<D, kBlockRowTiles>& S, char
 }
 
 template <int D, bool FA>
-__global__ __launch_bounds__(kBlock, 2) void block_lds_kernel(PartialArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[2 * LdsTile<D>::STAGE];
-  const int item = blockIdx.x / a.n_kvheads;
-  const int h = blockIdx.x - item * a.n_kvheads;
+__device__ __forceinline__ void block_lds_item(const PartialArgs& a, char* lds, int blk) {
+  const int item = blk / a.n_kvheads;
+  const int h = blk - item * a.n_kvheads;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int i = lane & 15, j = lane >> 4;
@@ -813,37 +831,53 @@ __global__ __launch_bounds__(kBlock, 2) void block_lds_kernel(PartialArgs a) {
 // Workgroup items, fp32 (GEMV path): one workgroup per item x kv-head; wave
 // w owns row pairs 2w, 2w + 8, ... over the whole chunk.
 template <typename T, int D, bool FA>
-__global__ __launch_bounds__(kBlock) void block_items_kernel(PartialArgs a) {
-  static_assert(std::is_same<T, float>::value, "bf16 workgroup items use block_lds_kernel");
-  const int item = blockIdx.x / a.n_kvheads;
-  const int h = blockIdx.x - item * a.n_kvheads;
+__device__ __forceinline__ void block_valu_item(const PartialArgs& a, int blk) {
+  const int item = blk / a.n_kvheads;
+  const int h = blk - item * a.n_kvheads;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const WorkItem it = a.items[item];
   for (int r = 2 * wave; r < it.nrows; r += 2 * kWaves) valu_wave_item<T, D, 2, FA>(a, it, h, r);
 }
 
-// Single-wave items (groups with few rows): each wave of the launch is one
-// item x kv-head and streams its whole chunk alone.
+// Single-wave items (groups with few rows): each wave is one item x kv-head
+// and streams its whole chunk alone.
 template <typename T, int D, bool FA>
-__global__ __launch_bounds__(kBlock, 2) void wave_items_kernel(PartialArgs a, int item0, int n_units) {
+__device__ __forceinline__ void wave_item(const PartialArgs& a, int item0, int n_units, int wblk) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int unit = blockIdx.x * kWaves + wave;
+  const int unit = wblk * kWaves + wave;
   if (unit >= n_units) return;
   const int item = item0 + unit / a.n_kvheads;
   const int h = unit - (unit / a.n_kvheads) * a.n_kvheads;
   const WorkItem it = a.items[item];
   if constexpr (std::is_same<T, __bf16>::value) {
-    if (it.nrows > kValuMaxRows) {
-      const int rt[1] = {0};
-      const bool on[1] = {true};
-      mfma_wave<D, 1, FA>(a, it, h, rt, on);
-      return;
-    }
-  }
-  if (it.nrows <= 1) {
+    // one 16-row MFMA tile even for one or two rows: the item is bound by
+    // its K/V stream, and the tile loop keeps twice the bytes in flight of
+    // the GEMV loop
+    const int rt[1] = {0};
+    const bool on[1] = {true};
+    mfma_wave<D, 1, FA>(a, it, h, rt, on);
+  } else if (it.nrows <= 1) {
     valu_wave_item<T, D, 1, FA>(a, it, h, 0);
   } else {
     for (int r = 0; r < it.nrows; r += 2) valu_wave_item<T, D, 2, FA>(a, it, h, r);
+  }
+}
+
+// The partial-attention launch: workgroups [0, n_block_wgs) take the
+// workgroup items (one per item x kv-head, longest items first as the
+// planner sorts them), the rest take the single-wave items, four units per
+// workgroup. One launch keeps both classes on the chip together without a
+// second stream.
+template <typename T, int D, bool FA>
+__global__ __launch_bounds__(kBlock, 2) void partial_kernel(PartialArgs a, int n_block_wgs, int n_units) {
+  constexpr bool kBf16 = std::is_same<T, __bf16>::value;
+  __shared__ __attribute__((aligned(16))) char lds[kBf16 ? 2 * LdsTile<D>::STAGE : 16];
+  const int blk = blockIdx.x;
+  if (blk < n_block_wgs) {
+    if constexpr (kBf16) block_lds_item<D, FA>(a, lds, blk);
+    else block_valu_item<T, D, FA>(a, blk);
+  } else {
+    wave_item<T, D, FA>(a, n_block_wgs / a.n_kvheads, n_units, blk - n_block_wgs);
   }
 }
 
@@ -934,59 +968,38 @@ __global__ void fill_kernel(float* p, int64_t n, float value) {
 }
 
 template <typename T, int D>
-void launch_block_t(const PartialArgs& a, int32_t n_block_items, hipStream_t s) {
-  const dim3 grid(unsigned(n_block_items) * a.n_kvheads), block(kBlock);
-  if constexpr (std::is_same<T, __bf16>::value) {
-    if (a.fast_addr) hipLaunchKernelGGL((block_lds_kernel<D, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((block_lds_kernel<D, false>), grid, block, 0, s, a);
-  } else {
-    if (a.fast_addr) hipLaunchKernelGGL((block_items_kernel<T, D, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((block_items_kernel<T, D, false>), grid, block, 0, s, a);
-  }
-}
-
-template <typename T, int D>
-void launch_wave_t(const PartialArgs& a, int32_t item0, int32_t n_wave_items, hipStream_t s) {
+void launch_partial_t(const PartialArgs& a, int32_t n_block_items, int32_t n_wave_items, hipStream_t s,
+                      KernelTimer t) {
+  const int n_block_wgs = n_block_items * a.n_kvheads;
   const int n_units = n_wave_items * a.n_kvheads;
-  const dim3 grid(unsigned((n_units + kWaves - 1) / kWaves)), block(kBlock);
-  if (a.fast_addr) hipLaunchKernelGGL((wave_items_kernel<T, D, true>), grid, block, 0, s, a, item0, n_units);
-  else hipLaunchKernelGGL((wave_items_kernel<T, D, false>), grid, block, 0, s, a, item0, n_units);
+  const dim3 grid(unsigned(n_block_wgs + (n_units + kWaves - 1) / kWaves)), block(kBlock);
+  if (a.fast_addr)
+    hipExtLaunchKernelGGL((partial_kernel<T, D, true>), grid, block, 0, s, t.start, t.stop, 0, a, n_block_wgs, n_units);
+  else
+    hipExtLaunchKernelGGL((partial_kernel<T, D, false>), grid, block, 0, s, t.start, t.stop, 0, a, n_block_wgs, n_units);
 }
 
 }  // namespace
 
-hipError_t launch_block_items(const PartialArgs& a, int32_t n_block_items, int dtype, int head_dim,
-                              hipStream_t s) {
-  if (n_block_items <= 0) return hipSuccess;
+hipError_t launch_partial(const PartialArgs& a, int32_t n_block_items, int32_t n_wave_items, int dtype,
+                          int head_dim, hipStream_t s, KernelTimer t) {
+  if (n_block_items + n_wave_items <= 0) return hipSuccess;
   if (dtype == 1) {
-    if (head_dim == 128) launch_block_t<__bf16, 128>(a, n_block_items, s);
-    else launch_block_t<__bf16, 64>(a, n_block_items, s);
+    if (head_dim == 128) launch_partial_t<__bf16, 128>(a, n_block_items, n_wave_items, s, t);
+    else launch_partial_t<__bf16, 64>(a, n_block_items, n_wave_items, s, t);
   } else {
-    if (head_dim == 128) launch_block_t<float, 128>(a, n_block_items, s);
-    else launch_block_t<float, 64>(a, n_block_items, s);
+    if (head_dim == 128) launch_partial_t<float, 128>(a, n_block_items, n_wave_items, s, t);
+    else launch_partial_t<float, 64>(a, n_block_items, n_wave_items, s, t);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_wave_items(const PartialArgs& a, int32_t item0, int32_t n_wave_items, int dtype,
-                             int head_dim, hipStream_t s) {
-  if (n_wave_items <= 0) return hipSuccess;
-  if (dtype == 1) {
-    if (head_dim == 128) launch_wave_t<__bf16, 128>(a, item0, n_wave_items, s);
-    else launch_wave_t<__bf16, 64>(a, item0, n_wave_items, s);
-  } else {
-    if (head_dim == 128) launch_wave_t<float, 128>(a, item0, n_wave_items, s);
-    else launch_wave_t<float, 64>(a, item0, n_wave_items, s);
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_reduce(const ReduceArgs& a, int head_dim, hipStream_t s) {
+hipError_t launch_reduce(const ReduceArgs& a, int head_dim, hipStream_t s, KernelTimer t) {
   const int64_t pairs = int64_t(a.n_queries) * a.n_qheads;
   if (pairs <= 0) return hipSuccess;
   const dim3 grid(unsigned((pairs + kWaves - 1) / kWaves)), block(kBlock);
-  if (head_dim == 128) hipLaunchKernelGGL(lse_reduce_kernel<128>, grid, block, 0, s, a);
-  else hipLaunchKernelGGL(lse_reduce_kernel<64>, grid, block, 0, s, a);
+  if (head_dim == 128) hipExtLaunchKernelGGL(lse_reduce_kernel<128>, grid, block, 0, s, t.start, t.stop, 0, a);
+  else hipExtLaunchKernelGGL(lse_reduce_kernel<64>, grid, block, 0, s, t.start, t.stop, 0, a);
   return hipGetLastError();
 }
 
