@@ -57,10 +57,10 @@ typedef enum { TA_F32 = 0, TA_BF16 = 1 } ta_dtype;
 /* Planner options. Any field left 0 takes its default. */
 typedef struct {
   int32_t ts_q;    /* query tile of the padding cost (default 16) */
-  int32_t ts_c;    /* context tile of the padding cost and chunk alignment (default 64) */
+  int32_t ts_c;    /* context tile of the padding cost (default 64) */
   int32_t gamma;   /* intermediate-result cost per query, in token units (default 32) */
   int32_t rb;      /* maximum rows (query x q-head-in-group) per work item (default 128) */
-  int32_t waves;   /* target busy waves per CU for the split rule (default 8) */
+  int32_t waves;   /* target busy waves per CU for the split rule (default 5) */
   int32_t floor_f; /* chunk length floor, in tokens per row (default 4) */
   int32_t ncu;     /* compute units (default: the current device's count; 256 if host_only) */
   int32_t no_split;/* 1 = never cut a group into KV chunks (default 0: split on) */
@@ -70,6 +70,8 @@ typedef struct {
   int32_t poison_workspace;  /* 1 = fill the workspace with NaN before every decode (testing) */
   int32_t stream_rows;       /* groups with at most this many rows (query x q-head-in-group)
                                 run as single-wave items (default 16; -1 = none) */
+  int32_t split_align;       /* the split's chunk length is a multiple of this many tokens
+                                (a multiple of 16; default 128: four 32-token tiles) */
 } ta_plan_opts;
 
 /* Paged K/V pools on the device. Element strides; head_dim is contiguous.
@@ -144,10 +146,10 @@ const char* tree_attn_last_error(void);
 
 /* Table ids for tree_attn_plan_export (all int32, row-major). */
 enum {
-  TA_T_PARAMS = 0,        /* [26]: version, n_nodes, n_queries, qpl, n_qheads, n_kvheads,
+  TA_T_PARAMS = 0,        /* [27]: version, n_nodes, n_queries, qpl, n_qheads, n_kvheads,
                              head_dim, page_size, ts_q, ts_c, gamma, rb, waves, floor_f, ncu,
                              split, forced, chunk_align, n_groups, n_chunks, n_items, n_slots,
-                             c_glob, n_runs, stream_rows, n_stream_items */
+                             c_glob, n_runs, stream_rows, n_stream_items, split_align */
   TA_T_EDGES = 1,         /* [n_nodes] f(parent -> v), 0 at the root */
   TA_T_NQ = 2,            /* [n_nodes] queries left in v's virtual node */
   TA_T_LCUM = 3,          /* [n_nodes] cumulative context length after merging */

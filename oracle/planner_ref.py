@@ -29,7 +29,9 @@ with the reasons in the design notes):
   page runs are this library's own, written out step by step below. Groups
   with at most ``stream_rows`` rows become single-wave stream items (one row
   block); larger groups become workgroup items (row blocks of ``rb``) whose
-  four waves share the chunk. The split rule counts capacity in waves.
+  four waves share the chunk. The split rule counts capacity in busy waves:
+  a single-wave stream as one, a workgroup block as 8/3 (its four waves
+  share each staged tile); chunk lengths are multiples of ``split_align``.
 
 Parity unpinned: the constants and the split rule (the page prints no plan,
 no cost value and no threshold); they are pinned only against this file.
@@ -40,8 +42,9 @@ from collections import deque
 
 import numpy as np
 
-FORMAT_VERSION = 2
+FORMAT_VERSION = 3
 WAVES_PER_WG = 4
+BLOCK_WAVE_WEIGHT3 = 8   # split rule: a workgroup block counts as 8/3 busy waves
 CHUNK_ALIGN = 16
 ITEM_FIXED_COST = 256
 
@@ -51,8 +54,8 @@ T_PARAMS, T_EDGES, T_NQ, T_LCUM, T_GROUPS, T_GROUP_QS, T_GROUP_VIS, T_CHUNKS, T_
 TABLE_NAMES = ["params", "edges", "nq", "lcum", "groups", "group_qs", "group_vis", "chunks",
                "items", "q_slot_ptr", "q_slots", "runs", "chunk_run_ptr", "bfs"]
 
-DEFAULTS = dict(ts_q=16, ts_c=64, gamma=32, rb=128, waves=8, floor_f=4, ncu=256, split=1,
-                stream_rows=16)
+DEFAULTS = dict(ts_q=16, ts_c=64, gamma=32, rb=128, waves=5, floor_f=4, ncu=256, split=1,
+                stream_rows=16, split_align=128)
 
 
 class PlanError(ValueError):
@@ -252,17 +255,17 @@ def build_plan(parent, node_len, node_page_ptr, node_page_ids, page_size, qpl,
             G["rb"] = _align_up(_cdiv(G["rows"], nb), 16 if rb % 16 == 0 else 1)
             G["nblocks"] = _cdiv(G["rows"], G["rb"])
     if o["split"]:
-        W = H * sum((1 if G["cls"] == 0 else WAVES_PER_WG) * G["nblocks"] * G["kv_len"]
+        W = H * sum((3 if G["cls"] == 0 else BLOCK_WAVE_WEIGHT3) * G["nblocks"] * G["kv_len"]
                     for G in groups)
-        U = _cdiv(W, o["ncu"] * o["waves"])
-        c_glob = max(ts_c, _align_up(U, ts_c))
+        U = _cdiv(W, o["ncu"] * o["waves"] * 3)
+        c_glob = max(o["split_align"], _align_up(U, o["split_align"]))
     else:
         c_glob = 0
     chunks = []
     for gi, G in enumerate(groups):
         kvl = G["kv_len"]
         if o["split"]:
-            cg = max(c_glob, _align_up(o["floor_f"] * min(G["rows"], G["rb"]), ts_c))
+            cg = max(c_glob, _align_up(o["floor_f"] * min(G["rows"], G["rb"]), o["split_align"]))
             nch = _cdiv(kvl, cg)
             csz = _align_up(_cdiv(kvl, nch), CHUNK_ALIGN)
             nch = _cdiv(kvl, csz)
@@ -341,7 +344,7 @@ def build_plan(parent, node_len, node_page_ptr, node_page_ids, page_size, qpl,
     params = [FORMAT_VERSION, n, n_q, qpl, n_qheads, n_kvheads, head_dim, page_size,
               ts_q, ts_c, gamma, rb, o["waves"], o["floor_f"], o["ncu"], o["split"],
               1 if force_edges is not None else 0, CHUNK_ALIGN, len(groups), len(chunks),
-              len(items), n_slots, c_glob, len(runs), o["stream_rows"], n_stream]
+              len(items), n_slots, c_glob, len(runs), o["stream_rows"], n_stream, o["split_align"]]
     gq, gv, gt = [], [], []
     for G in groups:
         gt.append([G["node"], G["top"], G["kv_len"], len(G["qs"]), len(gq), G["chunk_ptr"],

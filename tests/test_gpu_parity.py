@@ -80,7 +80,8 @@ def test_plan_invariance(k):
     rng = np.random.default_rng(k)
     variants = [dict(force_edges=[0] * n), dict(force_edges=[1] * n),
                 dict(force_edges=rng.integers(0, 2, n).tolist()), dict(split=False),
-                dict(ncu=1024, ts_c=16), dict(rb=32, floor_f=1), dict(waves=1, ncu=64)]
+                dict(ncu=1024, ts_c=16, split_align=16), dict(rb=32, floor_f=1), dict(waves=1, ncu=64),
+                dict(waves=8, split_align=64)]
     for kw in variants:
         got = _run(inst, dev, **kw)
         _check(got[rows], ref[rows], f"config {k} {kw if 'force_edges' not in kw else 'forced'}")
@@ -94,7 +95,7 @@ def test_random_trees(seed):
     ref = ta.decode_instance(inst)
     kw = {}
     if seed % 3 == 0:
-        kw = dict(ncu=512, ts_c=16)      # many small chunks, ragged tails
+        kw = dict(ncu=512, ts_c=16, split_align=16)      # many small chunks, ragged tails
     _check(_run(inst, **kw), ref, f"random tree {seed}")
 
 

@@ -55,7 +55,8 @@ def test_random_trees_bit_exact():
         elif r == 3:
             kw.update(split=0, ts_q=4, gamma=int(rng.integers(1, 200)))
         elif r == 4:
-            kw.update(waves=int(rng.integers(1, 8)), floor_f=int(rng.integers(1, 16)), ncu=16)
+            kw.update(waves=int(rng.integers(1, 8)), floor_f=int(rng.integers(1, 16)), ncu=16,
+                      split_align=int(rng.choice([16, 32, 48, 128])))
         _compare(inst, **kw)
 
 
@@ -76,11 +77,11 @@ def test_exported_symbols_match_header():
         assert hasattr(L, name), name
 
 
-def _plan_raw(parent, lens, ptr, ids, ps=16, qpl=1, hq=4, h=4, d=128, host_only=1):
+def _plan_raw(parent, lens, ptr, ids, ps=16, qpl=1, hq=4, h=4, d=128, host_only=1, **opt):
     L = _capi.lib()
     a = [np.ascontiguousarray(np.asarray(x, np.int32)) for x in (parent, lens, ptr, ids)]
     P = [x.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) for x in a]
-    opts = _capi.PlanOpts(host_only=host_only)
+    opts = _capi.PlanOpts(host_only=host_only, **opt)
     hnd = ctypes.c_void_p()
     st = L.tree_attn_plan(P[0], len(a[0]), P[1], P[2], P[3], ps, qpl, hq, h, d,
                           ctypes.byref(opts), ctypes.byref(hnd))
@@ -99,6 +100,8 @@ def _plan_raw(parent, lens, ptr, ids, ps=16, qpl=1, hq=4, h=4, d=128, host_only=
     (dict(ptr=[0, 1, 1]), _capi.TA_EINVAL),                 # page CSR size mismatch
     (dict(ids=[0, -3]), _capi.TA_EINVAL),                   # negative page id
     (dict(ps=0), _capi.TA_EINVAL),                          # page size
+    (dict(split_align=24), _capi.TA_EINVAL),                # split alignment not a multiple of 16
+    (dict(waves=-1), _capi.TA_EINVAL),                      # negative option
 ])
 def test_plan_error_codes(case, status):
     kw = dict(parent=[-1, 0], lens=[4, 4], ptr=[0, 1, 2], ids=[0, 1])

@@ -844,7 +844,7 @@ __device__ __forceinline__ void block_valu_item(const PartialArgs& a, int blk) {
 template <typename T, int D, bool FA>
 __device__ __forceinline__ void wave_item(const PartialArgs& a, int item0, int n_units, int wblk) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int unit = wblk * kWaves + wave;
+  const int unit = wblk * int(blockDim.x >> 6) + wave;
   if (unit >= n_units) return;
   const int item = item0 + unit / a.n_kvheads;
   const int h = unit - (unit / a.n_kvheads) * a.n_kvheads;
@@ -972,7 +972,10 @@ void launch_partial_t(const PartialArgs& a, int32_t n_block_items, int32_t n_wav
                       KernelTimer t) {
   const int n_block_wgs = n_block_items * a.n_kvheads;
   const int n_units = n_wave_items * a.n_kvheads;
-  const dim3 grid(unsigned(n_block_wgs + (n_units + kWaves - 1) / kWaves)), block(kBlock);
+  // single-wave units go two per workgroup when there are no workgroup
+  // items: the dispatcher then spreads them more evenly over the CUs
+  const int wpb = n_block_wgs == 0 ? 2 : kWaves;
+  const dim3 grid(unsigned(n_block_wgs + (n_units + wpb - 1) / wpb)), block(unsigned(wpb * 64));
   if (a.fast_addr)
     hipExtLaunchKernelGGL((partial_kernel<T, D, true>), grid, block, 0, s, t.start, t.stop, 0, a, n_block_wgs, n_units);
   else

@@ -21,8 +21,10 @@
 //      (query r / g, q-head r % g).
 //  P7  long-context split (FastTree review, section 3.3): a global chunk
 //      length sized so the launch gives about ncu * waves busy waves (a
-//      workgroup block counts its four waves), floored per group at floor_f
-//      tokens per row, balanced and 16-aligned.
+//      workgroup block counts as kBlockWaveWeight3 / 3 waves: its four waves
+//      share each staged tile), a multiple of split_align, floored per group
+//      at floor_f tokens per row; each group's chunks are then balanced and
+//      16-aligned.
 //  P8  work items: workgroup items first, then stream items, each class
 //      longest first (stable).
 //  P9  partial-result slots: group, then chunk, then query.
@@ -73,7 +75,7 @@ int build_plan(const int32_t* parent, int32_t n, const int32_t* node_len,
   if (page_size < 1 || page_size > 256)
     return fail(err, EINVAL_, "tree_attn_plan: page_size must be in 1..256");
   if (p.ts_q < 1 || p.ts_c < 1 || p.gamma < 0 || p.rb < 1 || p.waves < 1 || p.floor_f < 0 ||
-      p.ncu < 1 || p.stream_rows < 0)
+      p.ncu < 1 || p.stream_rows < 0 || p.split_align < 16 || p.split_align % 16)
     return fail(err, EINVAL_, "tree_attn_plan: invalid option value");
   int32_t root = -1;
   for (int32_t v = 0; v < n; ++v) {
@@ -224,10 +226,10 @@ int build_plan(const int32_t* parent, int32_t n, const int32_t* node_len,
   int64_t c_glob = 0;
   if (p.split) {
     int64_t W = 0;
-    for (auto& G : groups) W += int64_t(G.cls == 0 ? 1 : kWavesPerWG) * G.nblocks * G.kv_len;
+    for (auto& G : groups) W += int64_t(G.cls == 0 ? 3 : kBlockWaveWeight3) * G.nblocks * G.kv_len;
     W *= H;
-    const int64_t U = cdiv(W, int64_t(p.ncu) * p.waves);
-    c_glob = std::max<int64_t>(p.ts_c, align_up(U, p.ts_c));
+    const int64_t U = cdiv(W, int64_t(p.ncu) * p.waves * 3);
+    c_glob = std::max<int64_t>(p.split_align, align_up(U, p.split_align));
   }
   struct Chunk { int32_t group, t0, t1; };
   std::vector<Chunk> chunks;
@@ -236,7 +238,7 @@ int build_plan(const int32_t* parent, int32_t n, const int32_t* node_len,
     int64_t csz, nch;
     if (p.split) {
       const int64_t cg =
-          std::max<int64_t>(c_glob, align_up(int64_t(p.floor_f) * std::min(G.rows, G.rb), p.ts_c));
+          std::max<int64_t>(c_glob, align_up(int64_t(p.floor_f) * std::min(G.rows, G.rb), p.split_align));
       nch = cdiv(G.kv_len, cg);
       csz = align_up(cdiv(G.kv_len, nch), kChunkAlign);
       nch = cdiv(G.kv_len, csz);
@@ -352,7 +354,7 @@ int build_plan(const int32_t* parent, int32_t n, const int32_t* node_len,
               p.ts_q, p.ts_c, p.gamma, p.rb, p.waves, p.floor_f, p.ncu, p.split ? 1 : 0,
               p.force_edges ? 1 : 0, kChunkAlign, int32_t(groups.size()), int32_t(chunks.size()),
               int32_t(items.size()), n_slots, int32_t(c_glob), int32_t(T.runs.size() / 3),
-              p.stream_rows, n_stream};
+              p.stream_rows, n_stream, p.split_align};
   T.edges = f;
   T.nq = nQ;
   T.lcum.assign(n, 0);

@@ -9,17 +9,19 @@
 namespace ta {
 
 struct PlanParams {
-  int32_t ts_q = 16, ts_c = 64, gamma = 32, rb = 128, waves = 8, floor_f = 4, ncu = 256;
+  int32_t ts_q = 16, ts_c = 64, gamma = 32, rb = 128, waves = 5, floor_f = 4, ncu = 256;
+  int32_t split_align = 128;  // chunk lengths of the split are multiples of this
   int32_t split = 1;
   int32_t stream_rows = 16;  // groups with at most this many rows run as one-wave items
   const int8_t* force_edges = nullptr;
 };
 
-constexpr int32_t kFormatVersion = 2;
+constexpr int32_t kFormatVersion = 3;
 constexpr int32_t kWavesPerWG = 4;     // waves of a workgroup item
+constexpr int64_t kBlockWaveWeight3 = 8; // split rule: a workgroup block counts as 8/3 busy waves
 constexpr int32_t kChunkAlign = 16;     // chunk lengths are multiples of the MFMA token block
 constexpr int64_t kItemFixedCost = 256; // per-item cost proxy in row units (longest-first order)
-constexpr int32_t kParamsLen = 26;
+constexpr int32_t kParamsLen = 27;
 
 struct PlanTables {
   // exported (see include/tree_attn.h for the layouts)
