@@ -13,6 +13,8 @@ Infinity Cache would otherwise serve the whole tree. Inputs are resident in
 HBM before the timed region. Prints one JSON line.
 """
 import argparse
+import glob
+import hashlib
 import json
 import math
 import os
@@ -25,6 +27,52 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "tree-decode attn: µs/step + effective HBM GB/s (unique KV bytes) vs peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "partial_kernel_traffic.json")
+
+
+def source_hash():
+    """sha256 over the library's sources (kernels, planner, C ABI): the HBM
+    counters recorded under profiles/ hold only for the sources they were
+    taken on."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "tree_structured_shared_amd", "csrc", "*"))
+                   + glob.glob(os.path.join(ROOT, "include", "*.h")))
+    for f in files:
+        if f.endswith((".hip", ".cpp", ".h")):
+            h.update(os.path.basename(f).encode())
+            with open(f, "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def _traffic(workload):
+    """HBM bytes per partial-kernel launch from the recorded FETCH_SIZE /
+    WRITE_SIZE counters, each scaled by what the counter reads for a plain
+    copy of known size; None when no record matches these sources and this
+    workload."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != source_hash() or rec.get("workload") != workload:
+        return None
+    cal = rec["copy_calibration"]
+    f_scale = cal["bytes"] / (cal["fetch_size_kib"] * 1024.0)
+    w_scale = cal["bytes"] / (cal["write_size_kib"] * 1024.0)
+    return round(rec["fetch_size_kib"] * 1024.0 * f_scale + rec["write_size_kib"] * 1024.0 * w_scale)
+
+
+def _copy_calibration(mib):
+    """A plain device copy of known size, for scaling the HBM counters."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "copies": 3}), flush=True)
 
 
 def _cpu_baseline(inst, budget_s=12.0, max_reps=20):
@@ -62,12 +110,18 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--copies", type=int, default=0, help="KV pool copies (0 = enough for 1 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB on the device three times (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only: the method runs one layer's decode on one device "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        _copy_calibration(args.copy_calibration)
+        return
 
     import numpy as np
     import torch
@@ -190,7 +244,7 @@ def main():
             "unique_kv_bytes": unique,
             "kv_copies_rotated": copies,
             "plan": {"groups": int(P[18]), "chunks": int(P[19]), "items": int(P[20]),
-                     "slots": int(P[21]), "workgroups": int(P[20]) * inst.n_kvheads,
+                     "slots": int(P[21]), "units": int(P[20]) * inst.n_kvheads,
                      "edges_joined": int(plan.export("edges").sum())},
         },
         "kernels_us": {"partial_attn": round(part_us, 3), "lse_reduce": round(red_us, 3),
@@ -198,7 +252,8 @@ def main():
                        "partial_attn_warm": round(float(np.mean(pm_w)) * 1e3, 3),
                        "lse_reduce_warm": round(float(np.mean(rm_w)) * 1e3, 3)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": _traffic(inst.name), "traffic_unit": "bytes per launch",
                      "kernel": dominant, "kernel_us": round(part_us, 3)},
         "graph_us_per_step": round(graph_us, 3) if isinstance(graph_us, float) else graph_us,
         "planner_host_ms": {"tables_median": round(statistics.median(t_host) * 1e3, 3),
