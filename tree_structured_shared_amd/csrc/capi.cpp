@@ -39,7 +39,7 @@ struct ta_plan {
   void* d_tables = nullptr;  // one allocation for every device table
   ta::WorkItem* d_items = nullptr;
   int32_t *d_group_qs = nullptr, *d_group_vis = nullptr, *d_seg_tok = nullptr;
-  int32_t *d_q_slot_ptr = nullptr, *d_q_slots = nullptr;
+  int32_t *d_q_slot_ptr = nullptr, *d_slot_pos = nullptr;
   void* d_ws = nullptr;  // workspace: o_part | m_part | l_part
   float *d_o_part = nullptr, *d_m_part = nullptr, *d_l_part = nullptr;
   int64_t ws_bytes = 0;
@@ -110,10 +110,14 @@ ta_status upload(ta_plan* p) {
     w.flags = min_vis < ta::kHiLoMinPath ? 1 : 0;
     items[x] = w;
   }
+  // workspace position of every slot: query-major, so each query's partials
+  // are contiguous in path order and the reduction needs no slot list
+  std::vector<int32_t> slot_pos(T.q_slots.size(), 0);
+  for (size_t k = 0; k < T.q_slots.size(); ++k) slot_pos[T.q_slots[k]] = int32_t(k);
   const size_t sz_items = items.size() * sizeof(ta::WorkItem);
   const size_t sz_qs = T.group_qs.size() * 4, sz_vis = T.group_vis.size() * 4,
                sz_seg = T.seg_tok.size() * 4, sz_qsp = T.q_slot_ptr.size() * 4,
-               sz_qsl = T.q_slots.size() * 4;
+               sz_qsl = slot_pos.size() * 4;
   size_t off[6], total = 0;
   const size_t sizes[6] = {sz_items, sz_qs, sz_vis, sz_seg, sz_qsp, sz_qsl};
   for (int x = 0; x < 6; ++x) {
@@ -127,7 +131,7 @@ ta_status upload(ta_plan* p) {
   }
   std::vector<uint8_t> host(total, 0);
   const void* src[6] = {items.data(), T.group_qs.data(), T.group_vis.data(), T.seg_tok.data(),
-                        T.q_slot_ptr.data(), T.q_slots.data()};
+                        T.q_slot_ptr.data(), slot_pos.data()};
   for (int x = 0; x < 6; ++x)
     if (sizes[x]) std::memcpy(host.data() + off[x], src[x], sizes[x]);
   e = hipMemcpy(p->d_tables, host.data(), total, hipMemcpyHostToDevice);
@@ -138,7 +142,7 @@ ta_status upload(ta_plan* p) {
   p->d_group_vis = reinterpret_cast<int32_t*>(base + off[2]);
   p->d_seg_tok = reinterpret_cast<int32_t*>(base + off[3]);
   p->d_q_slot_ptr = reinterpret_cast<int32_t*>(base + off[4]);
-  p->d_q_slots = reinterpret_cast<int32_t*>(base + off[5]);
+  p->d_slot_pos = reinterpret_cast<int32_t*>(base + off[5]);
 
   const size_t n_pairs = size_t(T.n_slots) * p->n_qheads;
   const size_t sz_o = align256(n_pairs * p->head_dim * 4), sz_m = align256(n_pairs * 4);
@@ -284,6 +288,7 @@ ta_status tree_attn_decode(const void* q, ta_dtype q_dtype, const ta_paged_kv* k
   a.group_qs = plan->d_group_qs;
   a.group_vis = plan->d_group_vis;
   a.seg_tok = plan->d_seg_tok;
+  a.slot_pos = plan->d_slot_pos;
   a.q = q;
   a.k = kv->k;
   a.v = kv->v;
@@ -312,7 +317,6 @@ ta_status tree_attn_decode(const void* q, ta_dtype q_dtype, const ta_paged_kv* k
 
   ta::ReduceArgs r{};
   r.q_slot_ptr = plan->d_q_slot_ptr;
-  r.q_slots = plan->d_q_slots;
   r.o_part = plan->d_o_part;
   r.m_part = plan->d_m_part;
   r.l_part = plan->d_l_part;

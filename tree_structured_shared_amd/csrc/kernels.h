@@ -31,6 +31,8 @@ struct PartialArgs {
   const int32_t* group_qs;
   const int32_t* group_vis;
   const int32_t* seg_tok;  // (page << 8) | slot per segment token
+  const int32_t* slot_pos; // workspace position of each partial slot (query-major: query q's
+                           // slots, in path order, sit at [q_slot_ptr[q], q_slot_ptr[q + 1]))
   const void* q;
   const void* k;
   const void* v;
@@ -38,16 +40,15 @@ struct PartialArgs {
   int64_t sp_bytes, st_bytes;   // page and token strides in bytes
   int32_t fast_addr;            // 1: every pool byte offset fits 32 bits and both
                                 // byte strides fit 24 bits (24-bit multiplies)
-  float* o_part;   // [n_slots, n_qheads, D] unnormalised
-  float* m_part;   // [n_slots, n_qheads] running max, base-2 scaled units
-  float* l_part;   // [n_slots, n_qheads] sum of exp2(s - m)
+  float* o_part;   // [n_slots (by position), n_qheads, D] unnormalised
+  float* m_part;   // [n_slots (by position), n_qheads] running max, base-2 scaled units
+  float* l_part;   // [n_slots (by position), n_qheads] sum of exp2(s - m)
   int32_t n_qheads, n_kvheads, g;
   float scale_log2;  // softmax scale * log2(e)
 };
 
 struct ReduceArgs {
-  const int32_t* q_slot_ptr;
-  const int32_t* q_slots;
+  const int32_t* q_slot_ptr;  // query q's partials are at positions [q_slot_ptr[q], q_slot_ptr[q + 1])
   const float* o_part;
   const float* m_part;
   const float* l_part;

@@ -139,7 +139,8 @@ __device__ __forceinline__ float part_weight(float m, float M) {
 
 // ---------------------------------------------------------------------------
 // Rows of a work item. Row rr of the item is group row row0 + rr = (group
-// query qig, q-head-in-group hig); its partial goes to slot slot0 + qig.
+// query qig, q-head-in-group hig); its partial goes to slot slot0 + qig, stored
+// at that slot's workspace position.
 struct RowRef {
   int gq, vis, slot, qh;
   bool ok;
@@ -152,7 +153,7 @@ __device__ __forceinline__ RowRef row_ref(const PartialArgs& a, const WorkItem& 
     const int qig = grow / a.g, hig = grow - qig * a.g;
     r.gq = a.group_qs[it.q_ptr + qig];
     r.vis = a.group_vis[it.q_ptr + qig];
-    r.slot = it.slot0 + qig;
+    r.slot = a.slot_pos[it.slot0 + qig];
     r.qh = h * a.g + hig;
   }
   return r;
@@ -893,7 +894,7 @@ constexpr int kReduceGroups = 4;
 template <int D>
 __global__ __launch_bounds__(kBlock) void lse_reduce_kernel(ReduceArgs a) {
   constexpr int EPL = D / 16;      // output elements per lane
-  const int pair = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int pair = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (pair >= a.n_queries * a.n_qheads) return;
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, sub = lane & 15;
@@ -903,12 +904,13 @@ __global__ __launch_bounds__(kBlock) void lse_reduce_kernel(ReduceArgs a) {
   float acc[EPL];
 #pragma unroll
   for (int x = 0; x < EPL; ++x) acc[x] = 0.0f;
-  const int s0 = a.q_slot_ptr[q], s1 = a.q_slot_ptr[q + 1];
+  const int s0 = __builtin_amdgcn_readfirstlane(a.q_slot_ptr[q]);
+  const int s1 = __builtin_amdgcn_readfirstlane(a.q_slot_ptr[q + 1]);
   for (int b = s0 + g; b < s1; b += kReduceGroups * kReduceBatch) {
     int64_t pi[kReduceBatch];
 #pragma unroll
     for (int u = 0; u < kReduceBatch; ++u)
-      pi[u] = int64_t(a.q_slots[min(b + kReduceGroups * u, s1 - 1)]) * a.n_qheads + hq;
+      pi[u] = int64_t(min(b + kReduceGroups * u, s1 - 1)) * a.n_qheads + hq;
     float mv[kReduceBatch], lv[kReduceBatch];
     f32x4 ov[kReduceBatch][EPL / 4];
 #pragma unroll
