@@ -102,6 +102,61 @@ def _cpu_baseline(inst, budget_s=12.0, max_reps=20):
     }
 
 
+def streamed_kv_bytes(plan, inst):
+    """K/V bytes a plan's items stream: every item reads its chunk once per
+    kv-head (a group with several row blocks streams its chunks once per
+    block)."""
+    items, chunks = plan.export("items"), plan.export("chunks")
+    esize = 2 if str(inst.dtype).endswith("bfloat16") else 4
+    toks = int((chunks[items[:, 3], 2] - chunks[items[:, 3], 1]).sum())
+    return toks * inst.n_kvheads * inst.head_dim * 2 * esize
+
+
+def _ablation(args, inst, q, ks, vs, dev):
+    """The same kernels on the plan variants the pages compare: the greedy
+    edge assignment (FastTree), every edge 0 (one group per node: DeFT's
+    KV-guided grouping), every edge 1 (each leaf's queries stream their whole
+    path: query-separated decode), and greedy without the long-context split.
+    Each variant: wall time per step over the rotated KV copies."""
+    import numpy as np
+    import torch
+    from tree_structured_shared_amd import Plan
+    n = inst.n_nodes
+    variants = [("greedy", {}), ("all_0_kv_guided", dict(force_edges=[0] * n)),
+                ("all_1_query_separated", dict(force_edges=[1] * n)), ("greedy_no_split", dict(split=False))]
+    out = torch.empty((inst.n_queries, inst.n_qheads, inst.head_dim), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    ref = None
+    for name, kw in variants:
+        plan = Plan.for_instance(inst, **kw)
+        calls = [plan.launcher(q, ks[c], vs[c], out, stream.cuda_stream) for c in range(len(ks))]
+        for s in range(args.warmup):
+            calls[s % len(ks)]()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            calls[s % len(ks)]()
+        torch.cuda.synchronize()
+        us = (time.perf_counter() - t0) * 1e6 / args.steps
+        got = out.clone()
+        if ref is None:
+            ref = got
+        P = plan.export("params")
+        res[name] = {"us_per_step": round(us, 2),
+                     "effective_GBs": round(inst.unique_kv_bytes / us / 1e3, 1),
+                     "kv_bytes_streamed": streamed_kv_bytes(plan, inst),
+                     "groups": int(P[18]), "items": int(P[20]), "slots": int(P[21]),
+                     "edges_joined": int(plan.export("edges").sum()),
+                     "max_abs_diff_vs_greedy": float((got - ref).abs().max())}
+        plan.close()
+    base = res["greedy"]["us_per_step"]
+    for name in res:
+        res[name]["speedup_of_greedy"] = round(res[name]["us_per_step"] / base, 3)
+    print(json.dumps({"ablation": inst.name, "steps": args.steps, "unique_kv_bytes": inst.unique_kv_bytes,
+                      "variants": res}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,6 +167,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB on the device three times (counter calibration)")
+    ap.add_argument("--ablation", action="store_true",
+                    help="time the plan variants (greedy / all-0 / all-1 / no split) instead")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -136,6 +193,13 @@ def main():
     esize = 2 if inst.dtype == torch.bfloat16 else 4
     pool_bytes = 2 * inst.k_pool.numel() * esize
     copies = args.copies or max(2, math.ceil((1 << 30) / pool_bytes) + 1)
+
+    if args.ablation:
+        q = inst.q.to(dev)
+        ks = [inst.k_pool.to(dev) for _ in range(copies)]
+        vs = [inst.v_pool.to(dev) for _ in range(copies)]
+        _ablation(args, inst, q, ks, vs, dev)
+        return
 
     # planner host time (tables only, then the full plan with its one upload)
     t_host = []

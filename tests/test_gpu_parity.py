@@ -133,6 +133,22 @@ def test_edge_cases():
                 _check(_run(inst), ref, f"edge {par} {lens} qpl{qpl} ps{ps} {dtype}")
 
 
+@pytest.mark.parametrize("qpl", [8, 32, 64])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_speculative_trees(qpl, dtype):
+    """Larger speculative trees: 8-64 query tokens per leaf under the
+    leaf-local causal mask (a leaf's j-th query sees its leaf up to its own
+    position), with a shared prompt and a middle level."""
+    par = [-1, 0, 0, 1, 1, 2, 2, 2]
+    lens = [300, 40, 90, qpl + 5, 2 * qpl, qpl, qpl + 33, 3 * qpl + 1]
+    inst = synth.make_tree(par, lens, page_size=16, qpl=qpl, n_qheads=16, n_kvheads=4, head_dim=128,
+                           dtype=dtype, seed=qpl)
+    synth.fill_tensors(inst, seed=100 + qpl)
+    ref = ta.decode_instance(inst)
+    _check(_run(inst), ref, f"qpl {qpl} {dtype}")
+    _check(_run(inst, force_edges=[1] * inst.n_nodes), ref, f"qpl {qpl} {dtype} all-1")
+
+
 def test_max_rows_per_item():
     """A group with many rows (root of 300 queries x GQA 8 = 2400 rows) spans
     several row blocks."""
