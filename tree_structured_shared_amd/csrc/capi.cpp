@@ -113,10 +113,14 @@ ta_status upload(ta_plan* p) {
   // workspace position of every slot: query-major, so each query's partials
   // are contiguous in path order and the reduction needs no slot list
   std::vector<int32_t> slot_pos(T.q_slots.size(), 0);
+  // the page table carries kSegPad padding words: the workgroup tile loop
+  // reads a tile's words 16 at a time, up to 31 past a group's last token
+  std::vector<int32_t> seg_tok(T.seg_tok);
+  seg_tok.resize(seg_tok.size() + ta::kSegPad, 0);
   for (size_t k = 0; k < T.q_slots.size(); ++k) slot_pos[T.q_slots[k]] = int32_t(k);
   const size_t sz_items = items.size() * sizeof(ta::WorkItem);
   const size_t sz_qs = T.group_qs.size() * 4, sz_vis = T.group_vis.size() * 4,
-               sz_seg = T.seg_tok.size() * 4, sz_qsp = T.q_slot_ptr.size() * 4,
+               sz_seg = seg_tok.size() * 4, sz_qsp = T.q_slot_ptr.size() * 4,
                sz_qsl = slot_pos.size() * 4;
   size_t off[6], total = 0;
   const size_t sizes[6] = {sz_items, sz_qs, sz_vis, sz_seg, sz_qsp, sz_qsl};
@@ -130,7 +134,7 @@ ta_status upload(ta_plan* p) {
     return set_err(TA_ENOMEM, std::string("tree_attn_plan: hipMalloc(tables): ") + hipGetErrorString(e));
   }
   std::vector<uint8_t> host(total, 0);
-  const void* src[6] = {items.data(), T.group_qs.data(), T.group_vis.data(), T.seg_tok.data(),
+  const void* src[6] = {items.data(), T.group_qs.data(), T.group_vis.data(), seg_tok.data(),
                         T.q_slot_ptr.data(), slot_pos.data()};
   for (int x = 0; x < 6; ++x)
     if (sizes[x]) std::memcpy(host.data() + off[x], src[x], sizes[x]);

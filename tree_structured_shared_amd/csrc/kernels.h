@@ -26,11 +26,14 @@ struct WorkItem {
 // away, so such queries get the exact two-term (hi + lo) product.
 constexpr int32_t kHiLoMinPath = 1024;
 
+// Padding words after the last entry of the device page table.
+constexpr int32_t kSegPad = 32;
+
 struct PartialArgs {
   const WorkItem* items;
   const int32_t* group_qs;
   const int32_t* group_vis;
-  const int32_t* seg_tok;  // (page << 8) | slot per segment token
+  const int32_t* seg_tok;  // (page << 8) | slot per segment token (+ kSegPad padding words)
   const int32_t* slot_pos; // workspace position of each partial slot (query-major: query q's
                            // slots, in path order, sit at [q_slot_ptr[q], q_slot_ptr[q + 1]))
   const void* q;

@@ -685,29 +685,55 @@ struct LdsTile {
   }
 };
 
-// thread -> (part = K or V, token 0..31, first chunk): 128 threads per part
+// Direct-to-LDS tile loads (global_load_lds_dwordx4): lane l of one
+// instruction writes 16 bytes at the wave-uniform LDS base + 16 l, so one
+// instruction fills 1 KiB = RPK token rows. A tile's K and V take NI
+// instructions, NIW per wave. Lane l of an instruction covers token
+// t = blk * RPK + l / CH at LDS chunk position p = l % CH and fetches the
+// global chunk p ^ (t mod CH): the same XOR swizzle as LdsTile::off, with no
+// register staging.
 template <int D, bool FA>
-struct TileLoader {
-  static constexpr int NC = D / 32;  // 16-byte chunks per thread
+struct TileDma {
+  typedef LdsTile<D> L;
   typedef typename TokOff<FA>::type Off;
-  u32x4 r[NC];
-  int part, tok, c0;
-  const char* base;
-  __device__ __forceinline__ void init(const PartialArgs& a, int h) {
-    part = threadIdx.x >> 7;
-    const int idx = threadIdx.x & 127;
-    tok = idx & 31;
-    c0 = (idx >> 5) * NC;
-    base = pool_head(part ? a.v : a.k, a, h, 2);
+  static constexpr int CH = L::CH;
+  static constexpr int RPK = 1024 / L::ROW;           // token rows per instruction
+  static constexpr int NI = 2 * L::PART / 1024;       // instructions per tile (K and V)
+  static constexpr int NIW = NI / kWaves;             // per wave
+  static_assert(NI % kWaves == 0, "tile instructions split evenly over the waves");
+  static_assert(NIW * RPK == 16, "each wave moves the K or the V rows of 16 tokens");
+  const char* kb;
+  const char* vb;
+  int wave;
+  __device__ __forceinline__ void init(const PartialArgs& a, int h, int w) {
+    kb = pool_head(a.k, a, h, 2);
+    vb = pool_head(a.v, a, h, 2);
+    wave = w;
   }
-  __device__ __forceinline__ void load(int32_t sg, const PartialArgs& a) {
-    const Off off = TokOff<FA>::of(sg, a) + Off(c0 * 16);
+  // Wave w moves the K (w < 2) or V (w >= 2) rows of tokens 16 (w & 1) ..
+  // + 15 of the tile; e[] are their page-table words (wave-uniform, scalar
+  // loads: the wait for them never covers direct loads in flight). They go
+  // to lanes 0..15 of one register by v_writelane, and each lane takes its
+  // token's word by ds_bpermute (a per-lane select chain would be turned
+  // into a scratch lookup, a vector load).
+  __device__ __forceinline__ void issue(char* stage, const int32_t (&e)[16], const PartialArgs& a) const {
+    typedef __attribute__((address_space(3))) char lds_char;
+    const int lane = threadIdx.x & 63;
+    const int r = lane / CH, p = lane % CH;
+    int32_t words = 0;
 #pragma unroll
-    for (int x = 0; x < NC; ++x) r[x] = load_at<u32x4>(base, off + Off(16 * x));
-  }
-  __device__ __forceinline__ void store(char* stage) const {
+    for (int y = 0; y < 16; ++y) asm("v_writelane_b32 %0, %1, %2" : "+v"(words) : "s"(e[y]), "n"(y));
 #pragma unroll
-    for (int x = 0; x < NC; ++x) *reinterpret_cast<u32x4*>(stage + LdsTile<D>::off(part, tok, c0 + x)) = r[x];
+    for (int x = 0; x < NIW; ++x) {
+      const int m = wave * NIW + x;            // wave-uniform
+      const int part = m / (NI / 2), blk = m % (NI / 2);
+      const int32_t sg = __builtin_amdgcn_ds_bpermute((x * RPK + r) << 2, words);
+      const int t = blk * RPK + r;
+      const Off off = TokOff<FA>::of(sg, a) + Off(((p ^ (t & (CH - 1))) << 4));
+      const char* src = (part ? vb : kb) + off;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                       (lds_char*)(stage + part * L::PART + blk * 1024), 16, 0, 0);
+    }
   }
 };
 
@@ -764,32 +790,83 @@ __device__ __forceinline__ void lds_tile(MfmaState<D, NRTW>& S, const char* stag
   }
 }
 
-// The tile loop of a workgroup item: two LDS stages, the next tile in
-// flight in registers while the current one is computed, one barrier per
-// tile. NACT (row tiles this wave computes) and HILO are fixed per loop.
+// The tile loop of a workgroup item: kLdsStages LDS stages filled by direct
+// loads kLdsStages - 1 tiles ahead. Per tile: wait for this wave's own
+// loads of the tile (explicit vmcnt: the compiler does not order LDS reads
+// after direct loads), one barrier (every wave's part of the tile has landed
+// and every wave is done with the stage the next loads overwrite), the next
+// loads, then the compute. Inside the loop no register depends on a vector
+// load (the compiler would wait for every direct load in flight before its
+// first use): page-table words come by scalar loads. NACT (row tiles this
+// wave computes) and HILO are fixed per loop.
+constexpr int kLdsStages = 3;
+
+// s_waitcnt with vmcnt = n (< 16) and no wait on the other counters
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier for the LDS stages only: this wave's direct loads up to
+// the last N and all its LDS accesses retire, then s_barrier. (__syncthreads
+// also releases global memory, which waits for every direct load in flight.)
+// The clobber keeps the compiler from moving memory accesses across it.
+template <int N>
+__device__ __forceinline__ void lds_stage_barrier() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(N | (0x7 << 4) | (0x0 << 8));
+  asm volatile("s_barrier" ::: "memory");
+}
+
 template <int D, bool FA, int NACT, bool HILO>
 __device__ __forceinline__ void lds_stream(MfmaState<D, kBlockRowTiles>& S, char* lds, const PartialArgs& a,
                                            const WorkItem& it, int h, int i, int j) {
+  typedef TileDma<D, FA> Dma;
+  constexpr int ST = LdsTile<D>::STAGE;
   const int ntiles = (it.tok1 - it.tok0 + 31) >> 5;
-  const int32_t* st = a.seg_tok + it.seg_base;
-  const int last = it.tok1 - 1;
-  TileLoader<D, FA> ld;
-  ld.init(a, h);
-  ld.load(st[min(it.tok0 + ld.tok, last)], a);
-  int32_t sg_next = st[min(it.tok0 + 32 + ld.tok, last)];
-  ld.store(lds);
-  __syncthreads();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // this wave's 16 tokens of each tile: page-table words by scalar loads
+  // (the table carries 32 padding words, so the reads past a group's end
+  // stay inside it); tokens past the chunk take the chunk's last token
+  // the page table is read-only for the kernel's lifetime: read it through
+  // the constant address space, so the uniform reads become scalar loads
+  typedef const __attribute__((address_space(4))) int32_t cint32;
+  const cint32* st = (const cint32*)(a.seg_tok + __builtin_amdgcn_readfirstlane(it.seg_base));
+  const int last = __builtin_amdgcn_readfirstlane(it.tok1) - 1;
+  const int32_t e_last = st[last];
+  const int first16 = __builtin_amdgcn_readfirstlane(it.tok0) + (wave & 1) * 16;
+  auto words = [&](int n, int32_t (&e)[16]) {
+    const cint32* p = st + first16 + n * 32;
+    int32_t w[16];
+#pragma unroll
+    for (int y = 0; y < 16; ++y) w[y] = p[y];  // in the padded table: read unconditionally
+#pragma unroll
+    for (int y = 0; y < 16; ++y) e[y] = (first16 + n * 32 + y <= last) ? w[y] : e_last;
+  };
+  Dma dma;
+  dma.init(a, h, wave);
+  int32_t e[16];
+  // the unit's Q and row loads (and the previous unit's stores) retire
+  // here, so no register the loop reads waits on a vector load
+  wait_vmcnt<0>();
+  words(0, e);
+  dma.issue(lds, e, a);
+  words(1, e);
+  dma.issue(lds + ST, e, a);
+  int stage = 0;
   for (int n = 0; n < ntiles; ++n) {
-    const bool more = n + 1 < ntiles;
-    if (more) {
-      ld.load(sg_next, a);
-      sg_next = st[min(it.tok0 + (n + 2) * 32 + ld.tok, last)];
-    }
+    lds_stage_barrier<Dma::NIW>();  // this wave's loads of tile n landed (tile n + 1's in flight)
+    words(n + 2, e);
+    const int s2 = stage + 2 >= kLdsStages ? stage + 2 - kLdsStages : stage + 2;
+    dma.issue(lds + s2 * ST, e, a);
     if constexpr (NACT > 0)
-      lds_tile<D, kBlockRowTiles, NACT, HILO>(S, lds + (n & 1) * LdsTile<D>::STAGE, a, it, it.tok0 + n * 32, i, j);
-    if (more) ld.store(lds + ((n + 1) & 1) * LdsTile<D>::STAGE);
-    __syncthreads();
+      lds_tile<D, kBlockRowTiles, NACT, HILO>(S, lds + stage * ST, a, it, it.tok0 + n * 32, i, j);
+    stage = stage + 1 == kLdsStages ? 0 : stage + 1;
   }
+  // every wave's direct loads (the clamped ones past the end included) land
+  // before the stages are reused
+  lds_stage_barrier<0>();
 }
 
 template <int D, bool FA>
@@ -872,7 +949,7 @@ __device__ __forceinline__ void wave_item(const PartialArgs& a, int item0, int n
 template <typename T, int D, bool FA>
 __global__ __launch_bounds__(kBlock, 2) void partial_kernel(PartialArgs a, int n_block_wgs, int n_units) {
   constexpr bool kBf16 = std::is_same<T, __bf16>::value;
-  __shared__ __attribute__((aligned(16))) char lds[kBf16 ? 2 * LdsTile<D>::STAGE : 16];
+  __shared__ __attribute__((aligned(16))) char lds[kBf16 ? kLdsStages * LdsTile<D>::STAGE : 16];
   const int blk = blockIdx.x;
   if (blk < n_block_wgs) {
     if constexpr (kBf16) block_lds_item<D, FA>(a, lds, blk);
