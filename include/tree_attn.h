@@ -117,6 +117,32 @@ ta_status tree_attn_plan(const int32_t* parent, int32_t n_nodes, const int32_t* 
 ta_status tree_attn_decode(const void* q, ta_dtype q_dtype, const ta_paged_kv* kv,
                            const ta_plan* plan, float* out, void* hip_stream);
 
+/* Decode-loop update (plan reuse): after a decode step every leaf's new
+ * tokens are appended to its KV, and the next step's queries are each leaf's
+ * last queries_per_leaf tokens again. Leaf of rank r (ascending node id) grows
+ * by leaf_add[r] >= 0 tokens (leaf_add has one entry per leaf); the pages the
+ * growth needs, ceil(new_len / page_size) - ceil(old_len / page_size) per
+ * leaf, are taken in leaf-rank order from new_pages[n_new_pages] (device page
+ * ids, [0, 2^23); the caller has written their K/V). The edge assignment and
+ * so the context-query grouping are kept (FastTree review, section 3.2: the
+ * grouping is a per-tree decision; call tree_attn_plan again to regroup); the
+ * length-dependent steps (chunks, work items, slots, page table) are redone,
+ * and the exported tables then equal those of tree_attn_plan on the grown
+ * tree with force_edges = this plan's edges, except TA_T_PARAMS[16], which is
+ * 2 ("kept") where the plan was greedy.
+ * Device tables are updated in place, in order on hip_stream: enqueue the
+ * following decodes on the same stream. Only when the tables outgrow their
+ * allocation (they keep headroom after the first extend) or the page table is
+ * laid out afresh does the call wait for the device and upload them whole.
+ * *relaunch (may be NULL) is set to 1 when the decode's launch shape or a
+ * device address changed: a decode captured in a HIP graph must then be
+ * captured again; with 0 the captured graph stays valid. Do not call while a
+ * graph capture is in progress on hip_stream. host_only plans update their
+ * tables only. All-or-nothing on TA_EINVAL (counts, page ids); a failed device
+ * update (TA_EHIP, TA_ENOMEM) leaves the plan unusable for decode. */
+ta_status tree_attn_plan_extend(ta_plan* plan, const int32_t* leaf_add, const int32_t* new_pages,
+                                int64_t n_new_pages, void* hip_stream, int32_t* relaunch);
+
 /* Plan sizes. Any output pointer may be NULL. */
 ta_status tree_attn_plan_info(const ta_plan* plan, int32_t* n_queries, int64_t* workspace_bytes,
                               int32_t* n_items);
@@ -148,7 +174,8 @@ const char* tree_attn_last_error(void);
 enum {
   TA_T_PARAMS = 0,        /* [27]: version, n_nodes, n_queries, qpl, n_qheads, n_kvheads,
                              head_dim, page_size, ts_q, ts_c, gamma, rb, waves, floor_f, ncu,
-                             split, forced, chunk_align, n_groups, n_chunks, n_items, n_slots,
+                             split, edges (0 greedy, 1 forced, 2 kept by an extend),
+                             chunk_align, n_groups, n_chunks, n_items, n_slots,
                              c_glob, n_runs, stream_rows, n_stream_items, split_align */
   TA_T_EDGES = 1,         /* [n_nodes] f(parent -> v), 0 at the root */
   TA_T_NQ = 2,            /* [n_nodes] queries left in v's virtual node */
@@ -165,7 +192,11 @@ enum {
   TA_T_RUNS = 11,         /* [n_runs x 3] page id, first slot, tokens */
   TA_T_CHUNK_RUN_PTR = 12,/* [n_chunks + 1] */
   TA_T_BFS = 13,          /* [n_nodes] BFS order (children by ascending id) */
-  TA_T_COUNT = 14
+  TA_T_SEG_TOK = 14,      /* the page table the kernels read: word (page_id << 8) | slot of
+                             segment token t of group i at TA_T_GROUP_SEG[i] + t, t < kv_len;
+                             words past a group's kv_len are unused */
+  TA_T_GROUP_SEG = 15,    /* [n_groups] offset of each group's segment in TA_T_SEG_TOK */
+  TA_T_COUNT = 16
 };
 
 #ifdef __cplusplus

@@ -159,6 +159,62 @@ def fill_tensors(inst: TreeInstance, seed: int) -> TreeInstance:
     return inst
 
 
+def grow_leaves(inst: TreeInstance, leaf_add, seed: int):
+    """One decode-loop step of the tree: leaf of rank r gains leaf_add[r]
+    tokens at its end. The pages the growth needs are new pool pages (ids
+    n_pages.. shuffled by ``seed``), handed out in leaf-rank order; existing
+    K/V is kept, the new tokens' K and V are drawn as fp32 N(0,1) (K block
+    then V block, leaf-rank order) and a fresh Q for every query follows; the
+    new pages' unused slots carry the canaries. Returns (grown instance, new
+    page ids in the order the leaves take them)."""
+    leaf_add = np.asarray(leaf_add, np.int64)
+    has_child = np.zeros(inst.n_nodes, dtype=bool)
+    for v in range(inst.n_nodes):
+        if inst.parent[v] >= 0:
+            has_child[inst.parent[v]] = True
+    leaves = np.flatnonzero(~has_child)
+    assert len(leaf_add) == len(leaves) and (leaf_add >= 0).all()
+    ps = inst.page_size
+    rng = np.random.default_rng(seed)
+    old_len = inst.node_len.astype(np.int64)
+    new_len = old_len.copy()
+    new_len[leaves] += leaf_add
+    need = [int(-(-new_len[v] // ps) - (-(-old_len[v] // ps))) for v in leaves]
+    n_new = int(sum(need))
+    fresh = (inst.n_pages + rng.permutation(n_new)).astype(np.int32)
+    pages = [list(inst.node_page_ids[inst.node_page_ptr[v]:inst.node_page_ptr[v + 1]]) for v in range(inst.n_nodes)]
+    at = 0
+    for v, k in zip(leaves, need):
+        pages[v] += list(fresh[at:at + k])
+        at += k
+    ptr = np.zeros(inst.n_nodes + 1, np.int32)
+    ptr[1:] = np.cumsum([len(x) for x in pages])
+    ids = np.asarray([pg for x in pages for pg in x], np.int32)
+    out = dataclasses.replace(inst, node_len=new_len.astype(np.int32), node_page_ptr=ptr, node_page_ids=ids,
+                              n_pages=inst.n_pages + n_new, q=None, k_pool=None, v_pool=None)
+    if inst.k_pool is not None:
+        H, d = inst.n_kvheads, inst.head_dim
+        g = torch.Generator().manual_seed(seed)
+        n_tok = int(leaf_add.sum())
+        k_new = torch.randn((n_tok, H, d), generator=g, dtype=torch.float32).to(inst.dtype)
+        v_new = torch.randn((n_tok, H, d), generator=g, dtype=torch.float32).to(inst.dtype)
+        q = torch.randn((out.n_queries, inst.n_qheads, d), generator=g, dtype=torch.float32)
+        k = torch.zeros((n_new, ps, H, d), dtype=inst.dtype)
+        v = torch.full((n_new, ps, H, d), CANARY_V, dtype=torch.float32).to(inst.dtype)
+        k_pool = torch.cat([inst.k_pool, k]).contiguous()
+        v_pool = torch.cat([inst.v_pool, v]).contiguous()
+        x = 0
+        for v_id in leaves:
+            for t in range(int(old_len[v_id]), int(new_len[v_id])):
+                pg = pages[v_id][t // ps]
+                k_pool[pg, t % ps] = k_new[x]
+                v_pool[pg, t % ps] = v_new[x]
+                x += 1
+        out.q = q.to(inst.dtype).contiguous()
+        out.k_pool, out.v_pool = k_pool, v_pool
+    return out, fresh
+
+
 def make_tree(parent, node_len, *, page_size=16, qpl=1, n_qheads=4, n_kvheads=4, head_dim=64,
               dtype=torch.bfloat16, seed=0, contiguous=False, name="custom") -> TreeInstance:
     parent = np.asarray(parent, np.int32)

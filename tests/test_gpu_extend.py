@@ -1,0 +1,125 @@
+"""GPU: decode-loop plan reuse. After tree_attn_plan_extend (device tables
+updated in place on the decode stream, or uploaded whole when they outgrow
+their allocation) the decode of the grown tree matches the fp64 oracle, and
+a decode captured in a HIP graph replays the grown tree while extend reports
+no relaunch. Extends and decodes are enqueued back to back on one stream,
+without host synchronisation between them."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import tree_attention as ta
+from tree_structured_shared_amd import Plan
+
+pytestmark = pytest.mark.gpu
+TOL = 3e-3
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _check(got, ref, what):
+    got = got.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = np.nanmax(np.abs(got - ref))
+    _log(f"{what}: max-abs err {err:.3e}")
+    assert err <= TOL, f"{what}: max-abs err {err:.3e}"
+
+
+def _small_tree(dtype, qpl):
+    par = [-1, 0, 0, 1, 1, 2, 0]
+    lens = [300, 40, 70, 20, 33, 16, 5 + qpl]
+    inst = synth.make_tree(par, lens, page_size=16, qpl=qpl, n_qheads=16, n_kvheads=4, head_dim=128,
+                           dtype=dtype, seed=qpl)
+    return synth.fill_tensors(inst, seed=40 + qpl)
+
+
+@pytest.mark.parametrize("dtype,qpl", [(torch.bfloat16, 1), (torch.bfloat16, 4), (torch.float32, 2)])
+def test_extend_decode_matches_oracle(dtype, qpl):
+    inst = _small_tree(dtype, qpl)
+    plan = Plan.for_instance(inst, poison_workspace=True, ncu=64, ts_c=16, split_align=16)
+    rng = np.random.default_rng(qpl)
+    for step in range(7):
+        if step == 4:
+            add = rng.integers(200, 500, size=inst.n_leaves)     # outgrows the page-table slack
+        else:
+            add = np.full(inst.n_leaves, qpl) + (step % 2) * rng.integers(0, 40, size=inst.n_leaves)
+        inst, new_pages = synth.grow_leaves(inst, add, seed=100 * qpl + step)
+        relaunch = plan.extend(add, new_pages)
+        out = plan.decode(inst.q.cuda(), inst.k_pool.cuda(), inst.v_pool.cuda())
+        _check(out, ta.decode_instance(inst), f"{dtype} qpl {qpl} step {step} relaunch {relaunch}")
+    plan.close()
+
+
+def test_extend_config2_decode_loop():
+    """The multi-level prompt workload, one token per leaf per step."""
+    inst = synth.make_config(2)
+    plan = Plan.for_instance(inst, poison_workspace=True)
+    for step in range(3):
+        add = np.ones(inst.n_leaves, np.int64)
+        inst, new_pages = synth.grow_leaves(inst, add, seed=7 + step)
+        plan.extend(add, new_pages)
+        out = plan.decode(inst.q.cuda(), inst.k_pool.cuda(), inst.v_pool.cuda())
+        _check(out, ta.decode_instance(inst), f"config 2 step {step}")
+    plan.close()
+
+
+def test_extend_graph_replay():
+    """Pools, Q and out live at fixed addresses (pools with spare pages); the
+    captured decode replays the grown tree after every extend that reports
+    no relaunch, and is captured again when one does."""
+    inst = _small_tree(torch.bfloat16, 2)
+    spare = 256
+    shape = (inst.n_pages + spare,) + tuple(inst.k_pool.shape[1:])
+    k_dev = torch.zeros(shape, dtype=inst.dtype, device="cuda")
+    v_dev = torch.full(shape, synth.CANARY_V, dtype=torch.float32, device="cuda").to(inst.dtype)
+    q_dev = torch.empty(inst.q.shape, dtype=inst.dtype, device="cuda")
+    out = torch.empty((inst.n_queries, inst.n_qheads, inst.head_dim), dtype=torch.float32, device="cuda")
+
+    def load(x):
+        k_dev[:x.n_pages].copy_(x.k_pool)
+        v_dev[:x.n_pages].copy_(x.v_pool)
+        q_dev.copy_(x.q)
+
+    load(inst)
+    plan = Plan.for_instance(inst)
+    side = torch.cuda.Stream()
+
+    def capture():
+        g = torch.cuda.CUDAGraph()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            plan.decode(q_dev, k_dev, v_dev, out=out)
+            side.synchronize()
+            with torch.cuda.graph(g, stream=side):
+                plan.decode(q_dev, k_dev, v_dev, out=out)
+        torch.cuda.synchronize()
+        return g
+
+    g = capture()
+    replays = 0
+    for step in range(6):
+        add = np.ones(inst.n_leaves, np.int64) * (1 if step != 3 else 37)
+        inst, new_pages = synth.grow_leaves(inst, add, seed=500 + step)
+        assert inst.n_pages <= shape[0]
+        load(inst)
+        relaunch = plan.extend(add, new_pages)
+        if relaunch:
+            g = capture()
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        replayed = out.clone()
+        replays += 0 if relaunch else 1
+        eager = plan.decode(q_dev, k_dev, v_dev)
+        torch.cuda.synchronize()
+        assert torch.equal(replayed, eager), f"step {step}: replay differs from eager"
+        _check(replayed, ta.decode_instance(inst), f"graph step {step} relaunch {relaunch}")
+    assert replays >= 1, "no extend kept the captured graph valid"
+    plan.close()

@@ -58,14 +58,18 @@ class Plan:
                                int(queries_per_leaf), int(n_qheads), int(n_kvheads), int(head_dim),
                                ctypes.byref(opts), ctypes.byref(self._handle)))
         self.page_size = int(page_size)
+        self.qpl = int(queries_per_leaf)
         self.n_qheads = int(n_qheads)
         self.n_kvheads = int(n_kvheads)
         self.head_dim = int(head_dim)
         self.host_only = bool(host_only)
+        self._info()
+
+    def _info(self):
         nq = ctypes.c_int32()
         ws = ctypes.c_int64()
         ni = ctypes.c_int32()
-        check(L.tree_attn_plan_info(self._handle, ctypes.byref(nq), ctypes.byref(ws), ctypes.byref(ni)))
+        check(lib().tree_attn_plan_info(self._handle, ctypes.byref(nq), ctypes.byref(ws), ctypes.byref(ni)))
         self.n_queries, self.workspace_bytes, self.n_items = nq.value, ws.value, ni.value
 
     @classmethod
@@ -87,6 +91,26 @@ class Plan:
 
     def tables(self):
         return {k: self.export(k) for k in TABLE_IDS}
+
+    # -- decode loop ----------------------------------------------------------
+    def extend(self, leaf_add, new_pages=(), stream=None):
+        """Leaf of rank r grows by leaf_add[r] tokens (their K/V already in the
+        pools), taking the pages it needs from new_pages in leaf-rank order;
+        the grouping is kept (tree_attn_plan_extend). Returns True when a
+        captured decode graph must be captured again."""
+        n_leaves = self.n_queries // self.qpl
+        add, add_p = _i32(leaf_add)
+        pages, pages_p = _i32(new_pages)
+        if len(add) != n_leaves:
+            raise TreeAttnError(1, f"leaf_add must have one entry per leaf ({n_leaves})")
+        if stream is None and not self.host_only:
+            import torch
+            stream = torch.cuda.current_stream().cuda_stream
+        relaunch = ctypes.c_int32()
+        check(lib().tree_attn_plan_extend(self._handle, add_p, pages_p if len(pages) else None, len(pages),
+                                          ctypes.c_void_p(stream or 0), ctypes.byref(relaunch)))
+        self._info()
+        return bool(relaunch.value)
 
     # -- decode ---------------------------------------------------------------
     def decode(self, q, k_pool, v_pool, out=None, stream=None):

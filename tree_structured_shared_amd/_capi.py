@@ -13,14 +13,14 @@ STATUS_NAMES = {0: "TA_OK", 1: "TA_EINVAL", 2: "TA_ENOMEM", 3: "TA_EHIP", 4: "TA
 TABLE_IDS = {
     "params": 0, "edges": 1, "nq": 2, "lcum": 3, "groups": 4, "group_qs": 5, "group_vis": 6,
     "chunks": 7, "items": 8, "q_slot_ptr": 9, "q_slots": 10, "runs": 11, "chunk_run_ptr": 12,
-    "bfs": 13,
+    "bfs": 13, "seg_tok": 14, "group_seg": 15,
 }
 TABLE_COLS = {"groups": 8, "chunks": 3, "items": 5, "runs": 3}
 
 EXPORTED_SYMBOLS = [
     "tree_attn_plan", "tree_attn_decode", "tree_attn_plan_info", "tree_attn_plan_export",
     "tree_attn_timing_enable", "tree_attn_timing_read", "tree_attn_plan_destroy",
-    "tree_attn_last_error",
+    "tree_attn_last_error", "tree_attn_plan_extend",
 ]
 
 
@@ -71,6 +71,8 @@ def lib():
     L.tree_attn_decode.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(PagedKV),
                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     L.tree_attn_decode.restype = ctypes.c_int
+    L.tree_attn_plan_extend.argtypes = [ctypes.c_void_p, i32p, i32p, ctypes.c_int64, ctypes.c_void_p, i32p]
+    L.tree_attn_plan_extend.restype = ctypes.c_int
     L.tree_attn_plan_info.argtypes = [ctypes.c_void_p, i32p, ctypes.POINTER(ctypes.c_int64), i32p]
     L.tree_attn_plan_info.restype = ctypes.c_int
     L.tree_attn_plan_export.argtypes = [ctypes.c_void_p, ctypes.c_int32, i32p,

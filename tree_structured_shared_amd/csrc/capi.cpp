@@ -31,18 +31,35 @@ ta_status hip_err(hipError_t e, const char* where) {
 }  // namespace
 
 struct ta_plan {
+  ta::PlanState S;  // what a decode-loop extend reuses
   ta::PlanTables T;
   int32_t host_only = 0, head_dim = 0, n_qheads = 0, n_kvheads = 0, g = 1, page_size = 0, qpl = 0;
   float scale = 0.0f;
   int32_t poison = 0;
   int device = -1;
-  void* d_tables = nullptr;  // one allocation for every device table
+  // Device tables, one allocation of kRegions regions (word offsets / capacities):
+  // work items, group query ids, visible prefixes, page table (+ kSegPad), slot CSR,
+  // slot positions.
+  void* d_tables = nullptr;
+  size_t reg_off[6] = {}, reg_cap[6] = {}, tables_words = 0;
   ta::WorkItem* d_items = nullptr;
   int32_t *d_group_qs = nullptr, *d_group_vis = nullptr, *d_seg_tok = nullptr;
   int32_t *d_q_slot_ptr = nullptr, *d_slot_pos = nullptr;
+  // host copies of what the device holds in the item and slot-position regions
+  std::vector<ta::WorkItem> h_items;
+  std::vector<int32_t> h_slot_pos, h_vis, h_q_slot_ptr;
   void* d_ws = nullptr;  // workspace: o_part | m_part | l_part
   float *d_o_part = nullptr, *d_m_part = nullptr, *d_l_part = nullptr;
-  int64_t ws_bytes = 0;
+  int64_t ws_bytes = 0, ws_cap = 0;
+  // decode-loop updates: pinned host staging (two, alternating; an event marks
+  // when the copy out of each has run) and one device staging buffer
+  int32_t* h_stage[2] = {nullptr, nullptr};
+  size_t h_stage_cap[2] = {0, 0};
+  hipEvent_t stage_done[2] = {nullptr, nullptr};
+  bool stage_used[2] = {false, false};
+  int32_t stage_next = 0;
+  int32_t* d_stage = nullptr;
+  size_t d_stage_cap = 0;
   // 4 per timed decode: start/stop of the partial kernel and of the reduction
   std::vector<hipEvent_t> ev;
   int32_t timing_cap = 0, timing_n = 0;
@@ -52,6 +69,10 @@ namespace {
 
 const std::vector<int32_t>* table_ptr(const ta_plan* p, int32_t id) {
   const ta::PlanTables& T = p->T;
+  if ((id == TA_T_RUNS || id == TA_T_CHUNK_RUN_PTR) && !T.runs_valid) {
+    ta_plan* mp = const_cast<ta_plan*>(p);  // page runs are expanded on first export
+    ta::plan_runs(mp->S, mp->T);
+  }
   switch (id) {
     case TA_T_PARAMS: return &T.params;
     case TA_T_EDGES: return &T.edges;
@@ -67,6 +88,8 @@ const std::vector<int32_t>* table_ptr(const ta_plan* p, int32_t id) {
     case TA_T_RUNS: return &T.runs;
     case TA_T_CHUNK_RUN_PTR: return &T.chunk_run_ptr;
     case TA_T_BFS: return &T.bfs;
+    case TA_T_SEG_TOK: return &T.seg_tok;
+    case TA_T_GROUP_SEG: return &T.group_seg_base;
     default: return nullptr;
   }
 }
@@ -75,14 +98,27 @@ void free_device(ta_plan* p) {
   if (p->host_only) return;
   for (hipEvent_t e : p->ev) (void)hipEventDestroy(e);
   p->ev.clear();
+  for (int x = 0; x < 2; ++x) {
+    if (p->stage_done[x]) (void)hipEventDestroy(p->stage_done[x]);
+    if (p->h_stage[x]) (void)hipHostFree(p->h_stage[x]);
+    p->stage_done[x] = nullptr;
+    p->h_stage[x] = nullptr;
+  }
+  if (p->d_stage) (void)hipFree(p->d_stage);
   if (p->d_tables) (void)hipFree(p->d_tables);
   if (p->d_ws) (void)hipFree(p->d_ws);
   p->d_tables = p->d_ws = nullptr;
+  p->d_stage = nullptr;
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+inline size_t align64w(size_t words) { return (words + 63) & ~size_t(63); }  // 256-byte regions
+constexpr int kWordsPerItem = int(sizeof(ta::WorkItem) / 4);
 
-ta_status upload(ta_plan* p) {
+// Device forms of the plan's tables: work items in launch order and the
+// workspace position of every slot (query-major, so each query's partials
+// are contiguous in path order and the reduction needs no slot list).
+void device_forms(ta_plan* p) {
   const ta::PlanTables& T = p->T;
   // visible tokens of each query over its whole path (sum over its groups)
   std::vector<int64_t> q_vis(T.n_queries, 0);
@@ -90,8 +126,7 @@ ta_status upload(ta_plan* p) {
     const int32_t* G = &T.groups[8 * gi];
     for (int32_t x = 0; x < G[3]; ++x) q_vis[T.group_qs[G[4] + x]] += T.group_vis[G[4] + x];
   }
-  // work items in launch order
-  std::vector<ta::WorkItem> items(T.n_items);
+  p->h_items.resize(T.n_items);
   for (int32_t x = 0; x < T.n_items; ++x) {
     const int32_t gi = T.items[5 * x], r0 = T.items[5 * x + 1], nr = T.items[5 * x + 2],
                   ci = T.items[5 * x + 3];
@@ -108,58 +143,194 @@ ta_status upload(ta_plan* p) {
     for (int32_t qig = r0 / p->g; qig <= (r0 + nr - 1) / p->g; ++qig)
       min_vis = std::min(min_vis, q_vis[T.group_qs[G[4] + qig]]);
     w.flags = min_vis < ta::kHiLoMinPath ? 1 : 0;
-    items[x] = w;
+    p->h_items[x] = w;
   }
-  // workspace position of every slot: query-major, so each query's partials
-  // are contiguous in path order and the reduction needs no slot list
-  std::vector<int32_t> slot_pos(T.q_slots.size(), 0);
+  p->h_slot_pos.assign(T.q_slots.size(), 0);
+  for (size_t k = 0; k < T.q_slots.size(); ++k) p->h_slot_pos[T.q_slots[k]] = int32_t(k);
+}
+
+// Words each device region needs now.
+void region_sizes(const ta_plan* p, size_t (&w)[6]) {
+  const ta::PlanTables& T = p->T;
+  w[0] = size_t(T.n_items) * kWordsPerItem;
+  w[1] = T.group_qs.size();
+  w[2] = T.group_vis.size();
   // the page table carries kSegPad padding words: the workgroup tile loop
   // reads a tile's words 16 at a time, up to 31 past a group's last token
-  std::vector<int32_t> seg_tok(T.seg_tok);
-  seg_tok.resize(seg_tok.size() + ta::kSegPad, 0);
-  for (size_t k = 0; k < T.q_slots.size(); ++k) slot_pos[T.q_slots[k]] = int32_t(k);
-  const size_t sz_items = items.size() * sizeof(ta::WorkItem);
-  const size_t sz_qs = T.group_qs.size() * 4, sz_vis = T.group_vis.size() * 4,
-               sz_seg = seg_tok.size() * 4, sz_qsp = T.q_slot_ptr.size() * 4,
-               sz_qsl = slot_pos.size() * 4;
-  size_t off[6], total = 0;
-  const size_t sizes[6] = {sz_items, sz_qs, sz_vis, sz_seg, sz_qsp, sz_qsl};
-  for (int x = 0; x < 6; ++x) {
-    off[x] = total;
-    total += align256(sizes[x] ? sizes[x] : 1);
-  }
-  hipError_t e = hipMalloc(&p->d_tables, total);
-  if (e != hipSuccess) {
-    p->d_tables = nullptr;
-    return set_err(TA_ENOMEM, std::string("tree_attn_plan: hipMalloc(tables): ") + hipGetErrorString(e));
-  }
-  std::vector<uint8_t> host(total, 0);
-  const void* src[6] = {items.data(), T.group_qs.data(), T.group_vis.data(), seg_tok.data(),
-                        T.q_slot_ptr.data(), slot_pos.data()};
-  for (int x = 0; x < 6; ++x)
-    if (sizes[x]) std::memcpy(host.data() + off[x], src[x], sizes[x]);
-  e = hipMemcpy(p->d_tables, host.data(), total, hipMemcpyHostToDevice);
-  if (e != hipSuccess) return hip_err(e, "tree_attn_plan: hipMemcpy(tables)");
-  uint8_t* base = static_cast<uint8_t*>(p->d_tables);
-  p->d_items = reinterpret_cast<ta::WorkItem*>(base + off[0]);
-  p->d_group_qs = reinterpret_cast<int32_t*>(base + off[1]);
-  p->d_group_vis = reinterpret_cast<int32_t*>(base + off[2]);
-  p->d_seg_tok = reinterpret_cast<int32_t*>(base + off[3]);
-  p->d_q_slot_ptr = reinterpret_cast<int32_t*>(base + off[4]);
-  p->d_slot_pos = reinterpret_cast<int32_t*>(base + off[5]);
+  w[3] = T.seg_tok.size() + ta::kSegPad;
+  w[4] = T.q_slot_ptr.size();
+  w[5] = T.q_slots.size();
+}
 
-  const size_t n_pairs = size_t(T.n_slots) * p->n_qheads;
+int64_t workspace_need(const ta_plan* p) {
+  const size_t n_pairs = size_t(p->T.n_slots) * p->n_qheads;
+  return int64_t(align256(n_pairs * p->head_dim * 4) + 2 * align256(n_pairs * 4));
+}
+
+void set_workspace_ptrs(ta_plan* p) {
+  const size_t n_pairs = size_t(p->T.n_slots) * p->n_qheads;
   const size_t sz_o = align256(n_pairs * p->head_dim * 4), sz_m = align256(n_pairs * 4);
-  p->ws_bytes = int64_t(sz_o + 2 * sz_m);
-  e = hipMalloc(&p->d_ws, size_t(p->ws_bytes));
-  if (e != hipSuccess) {
-    p->d_ws = nullptr;
-    return set_err(TA_ENOMEM, std::string("tree_attn_plan: hipMalloc(workspace): ") + hipGetErrorString(e));
-  }
   uint8_t* wb = static_cast<uint8_t*>(p->d_ws);
   p->d_o_part = reinterpret_cast<float*>(wb);
   p->d_m_part = reinterpret_cast<float*>(wb + sz_o);
   p->d_l_part = reinterpret_cast<float*>(wb + sz_o + sz_m);
+}
+
+// (Re)allocate the workspace when it no longer fits; growth keeps headroom.
+// The caller has made sure no enqueued work uses the old one.
+ta_status ensure_workspace(ta_plan* p, bool headroom, bool* moved) {
+  p->ws_bytes = workspace_need(p);
+  if (p->d_ws && p->ws_bytes <= p->ws_cap) {
+    set_workspace_ptrs(p);
+    return TA_OK;
+  }
+  if (p->d_ws) (void)hipFree(p->d_ws);
+  p->d_ws = nullptr;
+  const int64_t cap = headroom ? p->ws_bytes + p->ws_bytes / 2 : p->ws_bytes;
+  hipError_t e = hipMalloc(&p->d_ws, size_t(cap));
+  if (e != hipSuccess) {
+    p->d_ws = nullptr;
+    p->ws_cap = 0;
+    return set_err(TA_ENOMEM, std::string("tree_attn_plan: hipMalloc(workspace): ") + hipGetErrorString(e));
+  }
+  p->ws_cap = cap;
+  *moved = true;
+  set_workspace_ptrs(p);
+  return TA_OK;
+}
+
+// Whole-table upload (plan creation, and an extend whose tables outgrew their
+// regions or whose page table was laid out afresh). The caller has made sure
+// no enqueued work reads the old tables.
+ta_status upload_full(ta_plan* p, bool headroom, bool* moved) {
+  const ta::PlanTables& T = p->T;
+  device_forms(p);
+  p->h_vis = T.group_vis;
+  p->h_q_slot_ptr = T.q_slot_ptr;
+  size_t need[6];
+  region_sizes(p, need);
+  bool fits = p->d_tables != nullptr;
+  for (int x = 0; x < 6; ++x) fits = fits && need[x] <= p->reg_cap[x];
+  if (!fits) {
+    if (p->d_tables) (void)hipFree(p->d_tables);
+    p->d_tables = nullptr;
+    size_t total = 0;
+    for (int x = 0; x < 6; ++x) {
+      const bool grows = x == 0 || x == 3 || x == 5;  // items, page table, slots
+      p->reg_cap[x] = align64w(std::max<size_t>(1, (headroom && grows) ? need[x] + need[x] / 2 : need[x]));
+      p->reg_off[x] = total;
+      total += p->reg_cap[x];
+    }
+    hipError_t e = hipMalloc(&p->d_tables, total * 4);
+    if (e != hipSuccess) {
+      p->d_tables = nullptr;
+      return set_err(TA_ENOMEM, std::string("tree_attn_plan: hipMalloc(tables): ") + hipGetErrorString(e));
+    }
+    p->tables_words = total;
+    *moved = true;
+  }
+  std::vector<int32_t> host(p->tables_words, 0);
+  const void* src[6] = {p->h_items.data(), T.group_qs.data(), T.group_vis.data(), T.seg_tok.data(),
+                        T.q_slot_ptr.data(), p->h_slot_pos.data()};
+  const size_t src_words[6] = {need[0], need[1], need[2], T.seg_tok.size(), need[4], need[5]};
+  for (int x = 0; x < 6; ++x)
+    if (src_words[x]) std::memcpy(host.data() + p->reg_off[x], src[x], src_words[x] * 4);
+  hipError_t e = hipMemcpy(p->d_tables, host.data(), p->tables_words * 4, hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_err(e, "tree_attn_plan: hipMemcpy(tables)");
+  int32_t* base = static_cast<int32_t*>(p->d_tables);
+  p->d_items = reinterpret_cast<ta::WorkItem*>(base + p->reg_off[0]);
+  p->d_group_qs = base + p->reg_off[1];
+  p->d_group_vis = base + p->reg_off[2];
+  p->d_seg_tok = base + p->reg_off[3];
+  p->d_q_slot_ptr = base + p->reg_off[4];
+  p->d_slot_pos = base + p->reg_off[5];
+  return ensure_workspace(p, headroom, moved);
+}
+
+ta_status upload(ta_plan* p) {
+  bool moved = false;
+  return upload_full(p, false, &moved);
+}
+
+// Decode-loop update of the device tables in place: the regions that changed
+// (and the page-table words of the grown segments) go through pinned staging
+// and one copy, then one kernel scatters them, all in order on `s`.
+ta_status upload_incremental(ta_plan* p, hipStream_t s) {
+  const ta::PlanTables& T = p->T;
+  std::vector<ta::WorkItem> old_items;
+  old_items.swap(p->h_items);
+  std::vector<int32_t> old_pos;
+  old_pos.swap(p->h_slot_pos);
+  device_forms(p);
+  // descriptors (dst word, words, src word) then the words themselves
+  std::vector<int32_t> desc, data;
+  auto add = [&](size_t dst, const int32_t* src, size_t n) {
+    if (n == 0) return;
+    desc.insert(desc.end(), {int32_t(dst), int32_t(n), int32_t(data.size())});
+    data.insert(data.end(), src, src + n);
+  };
+  const size_t w_items = size_t(T.n_items) * kWordsPerItem;
+  if (old_items.size() != p->h_items.size() ||
+      std::memcmp(old_items.data(), p->h_items.data(), w_items * 4) != 0)
+    add(p->reg_off[0], reinterpret_cast<const int32_t*>(p->h_items.data()), w_items);
+  if (T.group_vis != p->h_vis) add(p->reg_off[2], T.group_vis.data(), T.group_vis.size());
+  if (T.q_slot_ptr != p->h_q_slot_ptr) add(p->reg_off[4], T.q_slot_ptr.data(), T.q_slot_ptr.size());
+  if (old_pos != p->h_slot_pos) add(p->reg_off[5], p->h_slot_pos.data(), p->h_slot_pos.size());
+  for (size_t x = 0; x + 1 < T.seg_dirty.size(); x += 2)
+    add(p->reg_off[3] + size_t(T.seg_dirty[x]), T.seg_tok.data() + T.seg_dirty[x],
+        size_t(T.seg_dirty[x + 1] - T.seg_dirty[x]));
+  p->h_vis = T.group_vis;
+  p->h_q_slot_ptr = T.q_slot_ptr;
+  if (desc.empty()) return TA_OK;
+  const int32_t n_desc = int32_t(desc.size() / 3);
+  for (int32_t d = 0; d < n_desc; ++d) desc[3 * d + 2] += int32_t(desc.size());  // data after descriptors
+  const size_t words = desc.size() + data.size();
+  if (words >= size_t(INT32_MAX)) return set_err(TA_EINVAL, "tree_attn_plan_extend: update too large");
+  hipError_t e;
+  // device staging: grown only after the work that may still read it is done
+  if (words > p->d_stage_cap) {
+    if (p->d_stage) {
+      if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_err(e, "tree_attn_plan_extend: hipStreamSynchronize");
+      (void)hipFree(p->d_stage);
+      p->d_stage = nullptr;
+    }
+    const size_t cap = align64w(words + words / 2);
+    if ((e = hipMalloc(&p->d_stage, cap * 4)) != hipSuccess) {
+      p->d_stage = nullptr;
+      p->d_stage_cap = 0;
+      return hip_err(e, "tree_attn_plan_extend: hipMalloc(staging)");
+    }
+    p->d_stage_cap = cap;
+  }
+  // pinned host staging: this buffer's previous copy must have run
+  const int b = p->stage_next;
+  if (p->stage_used[b] && (e = hipEventSynchronize(p->stage_done[b])) != hipSuccess)
+    return hip_err(e, "tree_attn_plan_extend: hipEventSynchronize");
+  if (words > p->h_stage_cap[b]) {
+    if (p->h_stage[b]) (void)hipHostFree(p->h_stage[b]);
+    p->h_stage[b] = nullptr;
+    const size_t cap = align64w(words + words / 2);
+    if ((e = hipHostMalloc(reinterpret_cast<void**>(&p->h_stage[b]), cap * 4, hipHostMallocDefault)) != hipSuccess) {
+      p->h_stage[b] = nullptr;
+      p->h_stage_cap[b] = 0;
+      return hip_err(e, "tree_attn_plan_extend: hipHostMalloc(staging)");
+    }
+    p->h_stage_cap[b] = cap;
+  }
+  if (!p->stage_done[b] &&
+      (e = hipEventCreateWithFlags(&p->stage_done[b], hipEventDisableTiming)) != hipSuccess)
+    return hip_err(e, "tree_attn_plan_extend: hipEventCreate");
+  std::memcpy(p->h_stage[b], desc.data(), desc.size() * 4);
+  std::memcpy(p->h_stage[b] + desc.size(), data.data(), data.size() * 4);
+  if ((e = hipMemcpyAsync(p->d_stage, p->h_stage[b], words * 4, hipMemcpyHostToDevice, s)) != hipSuccess)
+    return hip_err(e, "tree_attn_plan_extend: hipMemcpyAsync");
+  if ((e = hipEventRecord(p->stage_done[b], s)) != hipSuccess)
+    return hip_err(e, "tree_attn_plan_extend: hipEventRecord");
+  p->stage_used[b] = true;
+  p->stage_next = b ^ 1;
+  if ((e = ta::launch_scatter(static_cast<int32_t*>(p->d_tables), int64_t(p->tables_words), p->d_stage, n_desc,
+                              s)) != hipSuccess)
+    return hip_err(e, "tree_attn_plan_extend: table update launch");
   return TA_OK;
 }
 
@@ -210,13 +381,14 @@ ta_status tree_attn_plan(const int32_t* parent, int32_t n_nodes, const int32_t* 
     if (!(scale >= 0.0f) || std::isinf(scale)) return set_err(TA_EINVAL, "tree_attn_plan: bad scale");
     p = new ta_plan;
     std::string err;
-    const int rc = ta::build_plan(parent, n_nodes, node_kv_len, node_page_ptr, node_page_ids,
-                                  page_size, queries_per_leaf, n_qheads, n_kvheads, head_dim, pp,
-                                  &p->T, &err);
+    const int rc = ta::plan_init(parent, n_nodes, node_kv_len, node_page_ptr, node_page_ids,
+                                 page_size, queries_per_leaf, n_qheads, n_kvheads, head_dim, pp,
+                                 &p->S, &err);
     if (rc != 0) {
       delete p;
       return set_err(ta_status(rc), err);
     }
+    ta::plan_layout(p->S, p->T);
     p->host_only = host_only;
     p->head_dim = head_dim;
     p->n_qheads = n_qheads;
@@ -243,6 +415,53 @@ ta_status tree_attn_plan(const int32_t* parent, int32_t n_nodes, const int32_t* 
   } catch (...) {
     delete p;
     return set_err(TA_EINVAL, "tree_attn_plan: unexpected failure");
+  }
+}
+
+ta_status tree_attn_plan_extend(ta_plan* plan, const int32_t* leaf_add, const int32_t* new_pages,
+                                int64_t n_new_pages, void* hip_stream, int32_t* relaunch) {
+  g_err.clear();
+  if (relaunch) *relaunch = 0;
+  if (!plan) return set_err(TA_EINVAL, "tree_attn_plan_extend: plan is NULL");
+  try {
+    if (!plan->host_only) {
+      int dev = -1;
+      hipError_t e = hipGetDevice(&dev);
+      if (e != hipSuccess) return hip_err(e, "tree_attn_plan_extend: hipGetDevice");
+      if (dev != plan->device)
+        return set_err(TA_EINVAL, "tree_attn_plan_extend: current device differs from the plan's");
+    }
+    const int32_t old_items = plan->T.n_items, old_stream = plan->T.n_stream_items, old_slots = plan->T.n_slots;
+    std::string err;
+    const int rc = ta::plan_extend(plan->S, leaf_add, new_pages, n_new_pages, &err);
+    if (rc != 0) return set_err(ta_status(rc), err);
+    ta::plan_layout(plan->S, plan->T);
+    if (plan->host_only) return TA_OK;
+    size_t need[6];
+    region_sizes(plan, need);
+    bool fits = !plan->T.seg_relaid;
+    for (int x = 0; x < 6; ++x) fits = fits && need[x] <= plan->reg_cap[x];
+    fits = fits && workspace_need(plan) <= plan->ws_cap;
+    bool moved = false;
+    ta_status st;
+    if (fits) {
+      st = upload_incremental(plan, static_cast<hipStream_t>(hip_stream));
+      set_workspace_ptrs(plan);
+      plan->ws_bytes = workspace_need(plan);
+    } else {
+      // regions outgrown or the page table laid out afresh: wait for every
+      // enqueued use of the old tables, then upload them whole (with headroom)
+      hipError_t e = hipDeviceSynchronize();
+      if (e != hipSuccess) return hip_err(e, "tree_attn_plan_extend: hipDeviceSynchronize");
+      st = upload_full(plan, true, &moved);
+    }
+    if (st != TA_OK) return st;
+    if (relaunch)
+      *relaunch = (moved || plan->T.n_items != old_items || plan->T.n_stream_items != old_stream ||
+                   plan->T.n_slots != old_slots) ? 1 : 0;
+    return TA_OK;
+  } catch (const std::bad_alloc&) {
+    return set_err(TA_ENOMEM, "tree_attn_plan_extend: host allocation failed");
   }
 }
 

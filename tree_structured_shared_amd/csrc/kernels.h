@@ -73,5 +73,9 @@ hipError_t launch_partial(const PartialArgs& a, int32_t n_block_items, int32_t n
                           int head_dim, hipStream_t s, KernelTimer t = {});
 hipError_t launch_reduce(const ReduceArgs& a, int head_dim, hipStream_t s, KernelTimer t = {});
 hipError_t launch_fill(float* p, int64_t n, float value, hipStream_t s);
+// Table update: stage holds n_desc descriptors (destination word, words,
+// source word in stage) followed by the words; each range is copied into
+// dst[0, dst_words). The host checks every range lies inside dst.
+hipError_t launch_scatter(int32_t* dst, int64_t dst_words, const int32_t* stage, int32_t n_desc, hipStream_t s);
 
 }  // namespace ta

@@ -41,6 +41,7 @@
 
 #include <hip/hip_ext.h>
 
+#include <algorithm>
 #include <type_traits>
 
 namespace ta {
@@ -1041,6 +1042,15 @@ __global__ __launch_bounds__(kBlock) void lse_reduce_kernel(ReduceArgs a) {
   }
 }
 
+// One workgroup per descriptor (grid-stride over descriptors).
+__global__ void scatter_kernel(int32_t* dst, int64_t dst_words, const int32_t* stage, int32_t n_desc) {
+  for (int32_t d = blockIdx.x; d < n_desc; d += gridDim.x) {
+    const int64_t to = stage[3 * d], n = stage[3 * d + 1], from = stage[3 * d + 2];
+    for (int64_t x = threadIdx.x; x < n; x += blockDim.x)
+      if (to + x < dst_words) dst[to + x] = stage[from + x];
+  }
+}
+
 __global__ void fill_kernel(float* p, int64_t n, float value) {
   for (int64_t x = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; x < n; x += int64_t(gridDim.x) * blockDim.x)
     p[x] = value;
@@ -1082,6 +1092,13 @@ hipError_t launch_reduce(const ReduceArgs& a, int head_dim, hipStream_t s, Kerne
   const dim3 grid(unsigned((pairs + kWaves - 1) / kWaves)), block(kBlock);
   if (head_dim == 128) hipExtLaunchKernelGGL(lse_reduce_kernel<128>, grid, block, 0, s, t.start, t.stop, 0, a);
   else hipExtLaunchKernelGGL(lse_reduce_kernel<64>, grid, block, 0, s, t.start, t.stop, 0, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter(int32_t* dst, int64_t dst_words, const int32_t* stage, int32_t n_desc, hipStream_t s) {
+  if (n_desc <= 0) return hipSuccess;
+  hipLaunchKernelGGL(scatter_kernel, dim3(unsigned(std::min(n_desc, 1024))), dim3(256), 0, s, dst, dst_words, stage,
+                     n_desc);
   return hipGetLastError();
 }
 
