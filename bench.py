@@ -13,6 +13,7 @@ Infinity Cache would otherwise serve the whole tree. Inputs are resident in
 HBM before the timed region. Prints one JSON line.
 """
 import argparse
+import gc
 import glob
 import hashlib
 import json
@@ -157,6 +158,87 @@ def _ablation(args, inst, q, ks, vs, dev):
                       "variants": res}), flush=True)
 
 
+def _decode_loop(args, inst, dev):
+    """Decode-loop plan reuse: W + K steps in which every leaf gains its
+    queries' worth of tokens (tree_attn_plan_extend, pages handed out from
+    spare pool pages) followed by one decode on the same stream, no host
+    synchronisation in between. Reports wall time per step, host time per
+    extend, the same decodes without growth, and the host time of planning
+    the grown tree from scratch (what each step would cost without reuse).
+    K/V of the new tokens is left at zero: this mode times, it does not check."""
+    import numpy as np
+    import torch
+    from tree_structured_shared_amd import Plan
+    K, W = args.steps, args.warmup
+    ps, qpl = inst.page_size, inst.qpl
+    has_child = np.zeros(inst.n_nodes, bool)
+    has_child[inst.parent[inst.parent >= 0]] = True
+    leaves = np.flatnonzero(~has_child)
+    lens = inst.node_len.astype(np.int64).copy()
+    next_page, sched = inst.n_pages, []
+    for _ in range(W + K):
+        pages = []
+        for v in leaves:
+            grow = -(-(lens[v] + qpl) // ps) - (-(-lens[v] // ps))
+            pages += list(range(next_page, next_page + grow))
+            next_page += grow
+            lens[v] += qpl
+        sched.append(np.asarray(pages, np.int32))
+    shape = (next_page,) + tuple(inst.k_pool.shape[1:])
+    k = torch.zeros(shape, dtype=inst.dtype, device=dev)
+    v = torch.zeros(shape, dtype=inst.dtype, device=dev)
+    k[:inst.n_pages].copy_(inst.k_pool)
+    v[:inst.n_pages].copy_(inst.v_pool)
+    q = inst.q.to(dev)
+    out = torch.empty((inst.n_queries, inst.n_qheads, inst.head_dim), dtype=torch.float32, device=dev)
+    plan = Plan.for_instance(inst)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    call = plan.launcher(q, k, v, out, stream)
+    add = np.full(len(leaves), qpl, np.int32)
+    for s in range(W):
+        plan.extend(add, sched[s], stream)
+        call()
+    torch.cuda.synchronize()
+    t_ext, relaunches = [], 0
+    gc.disable()
+    t0 = time.perf_counter()
+    for s in range(W, W + K):
+        a = time.perf_counter()
+        relaunches += int(plan.extend(add, sched[s], stream))
+        t_ext.append(time.perf_counter() - a)
+        call()
+    torch.cuda.synchronize()
+    loop_us = (time.perf_counter() - t0) * 1e6 / K
+    gc.enable()
+    t0 = time.perf_counter()
+    for s in range(K):
+        call()
+    torch.cuda.synchronize()
+    static_us = (time.perf_counter() - t0) * 1e6 / K
+    import dataclasses
+    g_inst = dataclasses.replace(inst, node_len=lens.astype(np.int32), q=None, k_pool=None, v_pool=None)
+    ptr = np.zeros(inst.n_nodes + 1, np.int32)
+    ptr[1:] = np.cumsum(-(-lens // ps))
+    g_inst.node_page_ptr = ptr
+    g_inst.node_page_ids = np.arange(int(ptr[-1]), dtype=np.int32)
+    t_fresh = []
+    for _ in range(20):
+        a = time.perf_counter()
+        Plan.for_instance(g_inst, host_only=True).close()
+        t_fresh.append(time.perf_counter() - a)
+    P = plan.export("params")
+    print(json.dumps({"decode_loop": inst.name, "steps": K, "warmup": W, "tokens_per_leaf_per_step": qpl,
+                      "us_per_step_with_extend": round(loop_us, 2), "us_per_step_no_growth": round(static_us, 2),
+                      "extend_host_us_median": round(statistics.median(t_ext) * 1e6, 2),
+                      "extend_host_us_p90": round(sorted(t_ext)[int(0.9 * (len(t_ext) - 1))] * 1e6, 2),
+                      "extend_host_us_max": round(max(t_ext) * 1e6, 2),
+                      "extends_needing_relaunch": relaunches,
+                      "fresh_plan_host_us_median": round(statistics.median(t_fresh) * 1e6, 2),
+                      "final_plan": {"items": int(P[20]), "slots": int(P[21]), "tokens": int(lens.sum())},
+                      "kv_cache": "warm (one pool, no rotation)"}), flush=True)
+    plan.close()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -169,6 +251,8 @@ def main():
                     help="only copy MIB MiB on the device three times (counter calibration)")
     ap.add_argument("--ablation", action="store_true",
                     help="time the plan variants (greedy / all-0 / all-1 / no split) instead")
+    ap.add_argument("--decode-loop", action="store_true",
+                    help="time decode steps with plan reuse (every leaf grows each step) instead")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -193,6 +277,10 @@ def main():
     esize = 2 if inst.dtype == torch.bfloat16 else 4
     pool_bytes = 2 * inst.k_pool.numel() * esize
     copies = args.copies or max(2, math.ceil((1 << 30) / pool_bytes) + 1)
+
+    if args.decode_loop:
+        _decode_loop(args, inst, dev)
+        return
 
     if args.ablation:
         q = inst.q.to(dev)
@@ -225,12 +313,15 @@ def main():
 
     K = args.steps
     # timed region: K back-to-back decode steps, each on its own KV copy
+    # (no collector pauses inside it)
+    gc.disable()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(K):
         calls[s % copies]()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gc.enable()
     ref_out = out.clone()
 
     # per-kernel device time: the library launches each kernel with HIP

@@ -109,7 +109,8 @@ class Plan:
         relaunch = ctypes.c_int32()
         check(lib().tree_attn_plan_extend(self._handle, add_p, pages_p if len(pages) else None, len(pages),
                                           ctypes.c_void_p(stream or 0), ctypes.byref(relaunch)))
-        self._info()
+        if relaunch.value or self.host_only:
+            self._info()
         return bool(relaunch.value)
 
     # -- decode ---------------------------------------------------------------

@@ -60,6 +60,7 @@ struct ta_plan {
   int32_t stage_next = 0;
   int32_t* d_stage = nullptr;
   size_t d_stage_cap = 0;
+  bool sized_for_growth = false;  // the first extend gave every region and the workspace headroom
   // 4 per timed decode: start/stop of the partial kernel and of the reduction
   std::vector<hipEvent_t> ev;
   int32_t timing_cap = 0, timing_n = 0;
@@ -180,13 +181,13 @@ void set_workspace_ptrs(ta_plan* p) {
 // The caller has made sure no enqueued work uses the old one.
 ta_status ensure_workspace(ta_plan* p, bool headroom, bool* moved) {
   p->ws_bytes = workspace_need(p);
-  if (p->d_ws && p->ws_bytes <= p->ws_cap) {
+  if (p->d_ws && p->ws_bytes <= p->ws_cap && !(headroom && p->ws_cap < 2 * p->ws_bytes)) {
     set_workspace_ptrs(p);
     return TA_OK;
   }
   if (p->d_ws) (void)hipFree(p->d_ws);
   p->d_ws = nullptr;
-  const int64_t cap = headroom ? p->ws_bytes + p->ws_bytes / 2 : p->ws_bytes;
+  const int64_t cap = headroom ? 2 * p->ws_bytes : p->ws_bytes;
   hipError_t e = hipMalloc(&p->d_ws, size_t(cap));
   if (e != hipSuccess) {
     p->d_ws = nullptr;
@@ -209,7 +210,7 @@ ta_status upload_full(ta_plan* p, bool headroom, bool* moved) {
   p->h_q_slot_ptr = T.q_slot_ptr;
   size_t need[6];
   region_sizes(p, need);
-  bool fits = p->d_tables != nullptr;
+  bool fits = p->d_tables != nullptr && !headroom;  // growth always re-sizes
   for (int x = 0; x < 6; ++x) fits = fits && need[x] <= p->reg_cap[x];
   if (!fits) {
     if (p->d_tables) (void)hipFree(p->d_tables);
@@ -217,7 +218,7 @@ ta_status upload_full(ta_plan* p, bool headroom, bool* moved) {
     size_t total = 0;
     for (int x = 0; x < 6; ++x) {
       const bool grows = x == 0 || x == 3 || x == 5;  // items, page table, slots
-      p->reg_cap[x] = align64w(std::max<size_t>(1, (headroom && grows) ? need[x] + need[x] / 2 : need[x]));
+      p->reg_cap[x] = align64w(std::max<size_t>(1, (headroom && grows) ? 2 * need[x] : need[x]));
       p->reg_off[x] = total;
       total += p->reg_cap[x];
     }
@@ -276,9 +277,12 @@ ta_status upload_incremental(ta_plan* p, hipStream_t s) {
   if (T.group_vis != p->h_vis) add(p->reg_off[2], T.group_vis.data(), T.group_vis.size());
   if (T.q_slot_ptr != p->h_q_slot_ptr) add(p->reg_off[4], T.q_slot_ptr.data(), T.q_slot_ptr.size());
   if (old_pos != p->h_slot_pos) add(p->reg_off[5], p->h_slot_pos.data(), p->h_slot_pos.size());
-  for (size_t x = 0; x + 1 < T.seg_dirty.size(); x += 2)
-    add(p->reg_off[3] + size_t(T.seg_dirty[x]), T.seg_tok.data() + T.seg_dirty[x],
-        size_t(T.seg_dirty[x + 1] - T.seg_dirty[x]));
+  if (T.seg_relaid)  // page table laid out afresh (a growing segment used up its slack)
+    add(p->reg_off[3], T.seg_tok.data(), T.seg_tok.size());
+  else
+    for (size_t x = 0; x + 1 < T.seg_dirty.size(); x += 2)
+      add(p->reg_off[3] + size_t(T.seg_dirty[x]), T.seg_tok.data() + T.seg_dirty[x],
+          size_t(T.seg_dirty[x + 1] - T.seg_dirty[x]));
   p->h_vis = T.group_vis;
   p->h_q_slot_ptr = T.q_slot_ptr;
   if (desc.empty()) return TA_OK;
@@ -294,7 +298,7 @@ ta_status upload_incremental(ta_plan* p, hipStream_t s) {
       (void)hipFree(p->d_stage);
       p->d_stage = nullptr;
     }
-    const size_t cap = align64w(words + words / 2);
+    const size_t cap = align64w(std::max(2 * words, p->tables_words));
     if ((e = hipMalloc(&p->d_stage, cap * 4)) != hipSuccess) {
       p->d_stage = nullptr;
       p->d_stage_cap = 0;
@@ -309,7 +313,7 @@ ta_status upload_incremental(ta_plan* p, hipStream_t s) {
   if (words > p->h_stage_cap[b]) {
     if (p->h_stage[b]) (void)hipHostFree(p->h_stage[b]);
     p->h_stage[b] = nullptr;
-    const size_t cap = align64w(words + words / 2);
+    const size_t cap = align64w(std::max(2 * words, p->tables_words));
     if ((e = hipHostMalloc(reinterpret_cast<void**>(&p->h_stage[b]), cap * 4, hipHostMallocDefault)) != hipSuccess) {
       p->h_stage[b] = nullptr;
       p->h_stage_cap[b] = 0;
@@ -439,7 +443,7 @@ ta_status tree_attn_plan_extend(ta_plan* plan, const int32_t* leaf_add, const in
     if (plan->host_only) return TA_OK;
     size_t need[6];
     region_sizes(plan, need);
-    bool fits = !plan->T.seg_relaid;
+    bool fits = plan->sized_for_growth;
     for (int x = 0; x < 6; ++x) fits = fits && need[x] <= plan->reg_cap[x];
     fits = fits && workspace_need(plan) <= plan->ws_cap;
     bool moved = false;
@@ -449,11 +453,12 @@ ta_status tree_attn_plan_extend(ta_plan* plan, const int32_t* leaf_add, const in
       set_workspace_ptrs(plan);
       plan->ws_bytes = workspace_need(plan);
     } else {
-      // regions outgrown or the page table laid out afresh: wait for every
-      // enqueued use of the old tables, then upload them whole (with headroom)
+      // first extend, or regions outgrown: wait for every enqueued use of the
+      // old tables, then upload them whole with room to grow (2x)
       hipError_t e = hipDeviceSynchronize();
       if (e != hipSuccess) return hip_err(e, "tree_attn_plan_extend: hipDeviceSynchronize");
       st = upload_full(plan, true, &moved);
+      plan->sized_for_growth = true;
     }
     if (st != TA_OK) return st;
     if (relaunch)
