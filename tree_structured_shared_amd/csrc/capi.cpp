@@ -157,7 +157,7 @@ void region_sizes(const ta_plan* p, size_t (&w)[6]) {
   w[1] = T.group_qs.size();
   w[2] = T.group_vis.size();
   // the page table carries kSegPad padding words: the workgroup tile loop
-  // reads a tile's words 16 at a time, up to 31 past a group's last token
+  // reads page-table words unconditionally a few tiles past a group's end
   w[3] = T.seg_tok.size() + ta::kSegPad;
   w[4] = T.q_slot_ptr.size();
   w[5] = T.q_slots.size();

@@ -26,8 +26,15 @@ struct WorkItem {
 // away, so such queries get the exact two-term (hi + lo) product.
 constexpr int32_t kHiLoMinPath = 1024;
 
-// Padding words after the last entry of the device page table.
-constexpr int32_t kSegPad = 32;
+// LDS stages of the workgroup tile loop (16 KiB each at head_dim 128; the
+// loop keeps kLdsStages - 1 tiles of 32 tokens in flight).
+constexpr int kLdsStages = 3;
+
+// Padding words after the last entry of the device page table. The workgroup
+// tile loop reads each wave's 16 page-table words of a tile unconditionally,
+// kLdsStages - 1 tiles ahead, so its reads reach at most
+// 63 + 32 * (kLdsStages - 2) words past a group's last token.
+constexpr int32_t kSegPad = 32 * kLdsStages;
 
 struct PartialArgs {
   const WorkItem* items;

@@ -800,7 +800,7 @@ __device__ __forceinline__ void lds_tile(MfmaState<D, NRTW>& S, const char* stag
 // load (the compiler would wait for every direct load in flight before its
 // first use): page-table words come by scalar loads. NACT (row tiles this
 // wave computes) and HILO are fixed per loop.
-constexpr int kLdsStages = 3;
+static_assert(kSegPad >= 63 + 32 * (kLdsStages - 2) + 1, "page-table padding covers the look-ahead reads");
 
 // s_waitcnt with vmcnt = n (< 16) and no wait on the other counters
 template <int N>
@@ -851,15 +851,17 @@ __device__ __forceinline__ void lds_stream(MfmaState<D, kBlockRowTiles>& S, char
   // the unit's Q and row loads (and the previous unit's stores) retire
   // here, so no register the loop reads waits on a vector load
   wait_vmcnt<0>();
-  words(0, e);
-  dma.issue(lds, e, a);
-  words(1, e);
-  dma.issue(lds + ST, e, a);
+#pragma unroll
+  for (int t = 0; t < kLdsStages - 1; ++t) {
+    words(t, e);
+    dma.issue(lds + t * ST, e, a);
+  }
   int stage = 0;
   for (int n = 0; n < ntiles; ++n) {
-    lds_stage_barrier<Dma::NIW>();  // this wave's loads of tile n landed (tile n + 1's in flight)
-    words(n + 2, e);
-    const int s2 = stage + 2 >= kLdsStages ? stage + 2 - kLdsStages : stage + 2;
+    // this wave's loads of tile n landed (those of the kLdsStages - 2 tiles after it in flight)
+    lds_stage_barrier<(kLdsStages - 2) * Dma::NIW>();
+    words(n + kLdsStages - 1, e);
+    const int s2 = stage == 0 ? kLdsStages - 1 : stage - 1;  // the stage of tile n - 1, done by every wave
     dma.issue(lds + s2 * ST, e, a);
     if constexpr (NACT > 0)
       lds_tile<D, kBlockRowTiles, NACT, HILO>(S, lds + stage * ST, a, it, it.tok0 + n * 32, i, j);
@@ -950,7 +952,9 @@ __device__ __forceinline__ void wave_item(const PartialArgs& a, int item0, int n
 template <typename T, int D, bool FA>
 __global__ __launch_bounds__(kBlock, 2) void partial_kernel(PartialArgs a, int n_block_wgs, int n_units) {
   constexpr bool kBf16 = std::is_same<T, __bf16>::value;
-  __shared__ __attribute__((aligned(16))) char lds[kBf16 ? kLdsStages * LdsTile<D>::STAGE : 16];
+  // the K/V stages of workgroup items (dynamic: launches without workgroup
+  // items reserve none)
+  extern __shared__ __attribute__((aligned(16))) char lds[];
   const int blk = blockIdx.x;
   if (blk < n_block_wgs) {
     if constexpr (kBf16) block_lds_item<D, FA>(a, lds, blk);
@@ -1065,10 +1069,14 @@ void launch_partial_t(const PartialArgs& a, int32_t n_block_items, int32_t n_wav
   // items: the dispatcher then spreads them more evenly over the CUs
   const int wpb = n_block_wgs == 0 ? 2 : kWaves;
   const dim3 grid(unsigned(n_block_wgs + (n_units + wpb - 1) / wpb)), block(unsigned(wpb * 64));
+  constexpr bool kBf16 = std::is_same<T, __bf16>::value;
+  const size_t lds = (kBf16 && n_block_wgs > 0) ? size_t(kLdsStages) * LdsTile<D>::STAGE : 0;
   if (a.fast_addr)
-    hipExtLaunchKernelGGL((partial_kernel<T, D, true>), grid, block, 0, s, t.start, t.stop, 0, a, n_block_wgs, n_units);
+    hipExtLaunchKernelGGL((partial_kernel<T, D, true>), grid, block, lds, s, t.start, t.stop, 0, a, n_block_wgs,
+                          n_units);
   else
-    hipExtLaunchKernelGGL((partial_kernel<T, D, false>), grid, block, 0, s, t.start, t.stop, 0, a, n_block_wgs, n_units);
+    hipExtLaunchKernelGGL((partial_kernel<T, D, false>), grid, block, lds, s, t.start, t.stop, 0, a, n_block_wgs,
+                          n_units);
 }
 
 }  // namespace
