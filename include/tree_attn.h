@@ -194,7 +194,8 @@ enum {
   TA_T_BFS = 13,          /* [n_nodes] BFS order (children by ascending id) */
   TA_T_SEG_TOK = 14,      /* the page table the kernels read: word (page_id << 8) | slot of
                              segment token t of group i at TA_T_GROUP_SEG[i] + t, t < kv_len;
-                             words past a group's kv_len are unused */
+                             the words after it, up to the next group's offset (at least 96),
+                             repeat tokens of the same segment (the kernels read ahead) */
   TA_T_GROUP_SEG = 15,    /* [n_groups] offset of each group's segment in TA_T_SEG_TOK */
   TA_T_COUNT = 16
 };

@@ -39,8 +39,11 @@ def _check_page_table(plan, inst):
         assert len(want) == kv_len
         got = seg_tok[bases[gi]:bases[gi] + kv_len]
         assert np.array_equal(got, want), f"group {gi}"
-        if gi + 1 < len(bases):
-            assert bases[gi] + kv_len <= bases[gi + 1]
+        # the words up to the next segment (the kernels read a few tiles past a
+        # segment's end) name written tokens of this segment, at least 96 of them
+        end = bases[gi + 1] if gi + 1 < len(bases) else len(seg_tok)
+        assert end - (bases[gi] + kv_len) >= 96, f"group {gi}: short guard"
+        assert set(seg_tok[bases[gi] + kv_len:end].tolist()) <= set(want), f"group {gi}: guard word"
 
 
 def _check_against_fresh(plan, inst, edges_mode, **kw):
@@ -137,4 +140,12 @@ def test_extend_errors_leave_plan_unchanged():
     grown, new_pages = synth.grow_leaves(inst, [1, 1], seed=4)
     plan.extend([1, 1], new_pages)
     _check_against_fresh(plan, grown, EDGES_KEPT)
+    plan.close()
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+def test_page_table_of_fresh_plans(k):
+    inst = synth.make_config(k, tensors=False)
+    plan = Plan.for_instance(inst, host_only=True)
+    _check_page_table(plan, inst)
     plan.close()

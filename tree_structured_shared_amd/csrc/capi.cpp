@@ -38,7 +38,7 @@ struct ta_plan {
   int32_t poison = 0;
   int device = -1;
   // Device tables, one allocation of kRegions regions (word offsets / capacities):
-  // work items, group query ids, visible prefixes, page table (+ kSegPad), slot CSR,
+  // work items, group query ids, visible prefixes, page table (guarded segments), slot CSR,
   // slot positions.
   void* d_tables = nullptr;
   size_t reg_off[6] = {}, reg_cap[6] = {}, tables_words = 0;
@@ -156,9 +156,7 @@ void region_sizes(const ta_plan* p, size_t (&w)[6]) {
   w[0] = size_t(T.n_items) * kWordsPerItem;
   w[1] = T.group_qs.size();
   w[2] = T.group_vis.size();
-  // the page table carries kSegPad padding words: the workgroup tile loop
-  // reads page-table words unconditionally a few tiles past a group's end
-  w[3] = T.seg_tok.size() + ta::kSegPad;
+  w[3] = T.seg_tok.size();  // every segment ends in the planner's guard words
   w[4] = T.q_slot_ptr.size();
   w[5] = T.q_slots.size();
 }

@@ -30,17 +30,18 @@ constexpr int32_t kHiLoMinPath = 1024;
 // loop keeps kLdsStages - 1 tiles of 32 tokens in flight).
 constexpr int kLdsStages = 3;
 
-// Padding words after the last entry of the device page table. The workgroup
-// tile loop reads each wave's 16 page-table words of a tile unconditionally,
-// kLdsStages - 1 tiles ahead, so its reads reach at most
-// 63 + 32 * (kLdsStages - 2) words past a group's last token.
-constexpr int32_t kSegPad = 32 * kLdsStages;
+// The workgroup tile loop reads each wave's 16 page-table words of a tile
+// unconditionally, kLdsStages - 1 tiles ahead, so its reads reach at most
+// 63 + 32 * (kLdsStages - 2) words past a group's last token; the planner's
+// per-segment guard (kSegGuard words repeating the segment's last token)
+// covers them.
+constexpr int32_t kLookAheadWords = 63 + 32 * (kLdsStages - 2) + 1;
 
 struct PartialArgs {
   const WorkItem* items;
   const int32_t* group_qs;
   const int32_t* group_vis;
-  const int32_t* seg_tok;  // (page << 8) | slot per segment token (+ kSegPad padding words)
+  const int32_t* seg_tok;  // (page << 8) | slot per segment token; each segment ends in guard words
   const int32_t* slot_pos; // workspace position of each partial slot (query-major: query q's
                            // slots, in path order, sit at [q_slot_ptr[q], q_slot_ptr[q + 1]))
   const void* q;

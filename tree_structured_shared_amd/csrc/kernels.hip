@@ -38,6 +38,7 @@
 // score exceeds it by more than 8 (log2 units), so rescaling is rare; l and o
 // always stay relative to the stored m.
 #include "kernels.h"
+#include "planner.h"
 
 #include <hip/hip_ext.h>
 
@@ -800,7 +801,7 @@ __device__ __forceinline__ void lds_tile(MfmaState<D, NRTW>& S, const char* stag
 // load (the compiler would wait for every direct load in flight before its
 // first use): page-table words come by scalar loads. NACT (row tiles this
 // wave computes) and HILO are fixed per loop.
-static_assert(kSegPad >= 63 + 32 * (kLdsStages - 2) + 1, "page-table padding covers the look-ahead reads");
+static_assert(kSegGuard >= kLookAheadWords, "the page-table guard covers the look-ahead reads");
 
 // s_waitcnt with vmcnt = n (< 16) and no wait on the other counters
 template <int N>
@@ -827,23 +828,19 @@ __device__ __forceinline__ void lds_stream(MfmaState<D, kBlockRowTiles>& S, char
   constexpr int ST = LdsTile<D>::STAGE;
   const int ntiles = (it.tok1 - it.tok0 + 31) >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // this wave's 16 tokens of each tile: page-table words by scalar loads
-  // (the table carries 32 padding words, so the reads past a group's end
-  // stay inside it); tokens past the chunk take the chunk's last token
-  // the page table is read-only for the kernel's lifetime: read it through
-  // the constant address space, so the uniform reads become scalar loads
+  // this wave's 16 tokens of each tile: page-table words by scalar loads.
+  // The page table is read-only for the kernel's lifetime: read it through
+  // the constant address space, so the uniform reads become scalar loads.
+  // Words past the chunk name other tokens of the segment, or (past the
+  // segment) its guard words, which repeat a written token: every load is of
+  // written K/V, and the softmax masks those tokens.
   typedef const __attribute__((address_space(4))) int32_t cint32;
   const cint32* st = (const cint32*)(a.seg_tok + __builtin_amdgcn_readfirstlane(it.seg_base));
-  const int last = __builtin_amdgcn_readfirstlane(it.tok1) - 1;
-  const int32_t e_last = st[last];
   const int first16 = __builtin_amdgcn_readfirstlane(it.tok0) + (wave & 1) * 16;
   auto words = [&](int n, int32_t (&e)[16]) {
     const cint32* p = st + first16 + n * 32;
-    int32_t w[16];
 #pragma unroll
-    for (int y = 0; y < 16; ++y) w[y] = p[y];  // in the padded table: read unconditionally
-#pragma unroll
-    for (int y = 0; y < 16; ++y) e[y] = (first16 + n * 32 + y <= last) ? w[y] : e_last;
+    for (int y = 0; y < 16; ++y) e[y] = p[y];
   };
   Dma dma;
   dma.init(a, h, wave);

@@ -380,7 +380,7 @@ void plan_layout(PlanState& S, PlanTables& T) {
       G.seg_base = int32_t(pos);
       G.seg_cap = int32_t(G.kv_len + ((S.extended && G.grows) ? seg_slack(G.kv_len) : 0));
       G.seg_filled = 0;
-      pos += G.seg_cap;
+      pos += G.seg_cap + kSegGuard;
     }
     T.seg_tok.assign(size_t(pos), 0);
   }
@@ -392,6 +392,11 @@ void plan_layout(PlanState& S, PlanTables& T) {
       fill_segment(S, G, G.seg_filled, G.kv_len, T.seg_tok);
       if (!relay) T.seg_dirty.insert(T.seg_dirty.end(), {G.seg_base + G.seg_filled, G.seg_base + G.kv_len});
       G.seg_filled = G.kv_len;
+    }
+    if (relay) {  // slack and guard repeat the last token (growth overwrites the slack in place)
+      const int32_t lastw = T.seg_tok[size_t(G.seg_base + G.kv_len - 1)];
+      std::fill(T.seg_tok.begin() + G.seg_base + G.kv_len, T.seg_tok.begin() + G.seg_base + G.seg_cap + kSegGuard,
+                lastw);
     }
   }
   // page runs per chunk: counted here (a run is the part of one page of one

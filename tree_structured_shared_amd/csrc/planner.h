@@ -21,6 +21,11 @@ constexpr int64_t kBlockWaveWeight3 = 8; // split rule: a workgroup block counts
 constexpr int32_t kChunkAlign = 16;     // chunk lengths are multiples of the MFMA token block
 constexpr int64_t kItemFixedCost = 256; // per-item cost proxy in row units (longest-first order)
 constexpr int32_t kParamsLen = 27;
+// Page-table words after each group's segment (and its slack) that repeat the
+// segment's last token: the kernels may read a few tiles of words past a
+// segment's end unconditionally, and every word they can reach names a token
+// the caller has written.
+constexpr int32_t kSegGuard = 96;
 // How the edge assignment was made (exported in the params table):
 constexpr int32_t kEdgesGreedy = 0;  // the greedy assignment on these lengths
 constexpr int32_t kEdgesForced = 1;  // given by the caller
@@ -33,7 +38,8 @@ struct PlanTables {
   bool runs_valid = false;  // runs / chunk_run_ptr are expanded on demand (plan_runs)
   // kernel-side expansions
   std::vector<int32_t> seg_tok;        // per group segment: (page_id << 8) | slot, one per token;
-                                       // a group's region may end in unused slack words
+                                       // each region ends in slack and kSegGuard words that
+                                       // repeat an earlier token of the segment
   std::vector<int32_t> group_seg_base; // offset of each group's segment in seg_tok
   // what the last plan_layout changed in seg_tok: everything (laid out afresh) or
   // the word ranges [seg_dirty[2i], seg_dirty[2i + 1])
