@@ -72,6 +72,9 @@ typedef struct {
                                 run as single-wave items (default 16; -1 = none) */
   int32_t split_align;       /* the split's chunk length is a multiple of this many tokens
                                 (a multiple of 16; default 128: four 32-token tiles) */
+  int32_t no_tile_join;      /* 1 = groups of 16 or more rows stay single-wave items (when
+                                at most stream_rows) even if the plan has workgroup items;
+                                default 0: they join the workgroup items */
 } ta_plan_opts;
 
 /* Paged K/V pools on the device. Element strides; head_dim is contiguous.
@@ -172,11 +175,12 @@ const char* tree_attn_last_error(void);
 
 /* Table ids for tree_attn_plan_export (all int32, row-major). */
 enum {
-  TA_T_PARAMS = 0,        /* [27]: version, n_nodes, n_queries, qpl, n_qheads, n_kvheads,
+  TA_T_PARAMS = 0,        /* [28]: version, n_nodes, n_queries, qpl, n_qheads, n_kvheads,
                              head_dim, page_size, ts_q, ts_c, gamma, rb, waves, floor_f, ncu,
                              split, edges (0 greedy, 1 forced, 2 kept by an extend),
                              chunk_align, n_groups, n_chunks, n_items, n_slots,
-                             c_glob, n_runs, stream_rows, n_stream_items, split_align */
+                             c_glob, n_runs, stream_rows, n_stream_items, split_align,
+                             tile_join */
   TA_T_EDGES = 1,         /* [n_nodes] f(parent -> v), 0 at the root */
   TA_T_NQ = 2,            /* [n_nodes] queries left in v's virtual node */
   TA_T_LCUM = 3,          /* [n_nodes] cumulative context length after merging */

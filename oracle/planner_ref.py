@@ -29,7 +29,9 @@ with the reasons in the design notes):
   page runs are this library's own, written out step by step below. Groups
   with at most ``stream_rows`` rows become single-wave stream items (one row
   block); larger groups become workgroup items (row blocks of ``rb``) whose
-  four waves share the chunk. The split rule counts capacity in busy waves:
+  four waves share the chunk. When a plan has workgroup items, the groups
+  that fill a whole 16-row tile join them (``tile_join``): one launch then
+  holds a single item class wherever the rows allow it. The split rule counts capacity in busy waves:
   a single-wave stream as one, a workgroup block as 8/3 (its four waves
   share each staged tile); chunk lengths are multiples of ``split_align``.
 
@@ -42,7 +44,8 @@ from collections import deque
 
 import numpy as np
 
-FORMAT_VERSION = 3
+FORMAT_VERSION = 4
+TILE_ROWS = 16          # rows of one MFMA row tile
 WAVES_PER_WG = 4
 BLOCK_WAVE_WEIGHT3 = 8   # split rule: a workgroup block counts as 8/3 busy waves
 CHUNK_ALIGN = 16
@@ -55,7 +58,7 @@ TABLE_NAMES = ["params", "edges", "nq", "lcum", "groups", "group_qs", "group_vis
                "items", "q_slot_ptr", "q_slots", "runs", "chunk_run_ptr", "bfs"]
 
 DEFAULTS = dict(ts_q=16, ts_c=64, gamma=32, rb=128, waves=5, floor_f=4, ncu=256, split=1,
-                stream_rows=16, split_align=128)
+                stream_rows=16, split_align=128, tile_join=1)
 
 
 class PlanError(ValueError):
@@ -107,6 +110,8 @@ def build_plan(parent, node_len, node_page_ptr, node_page_ids, page_size, qpl,
             o[k] = int(v)
     if "split" in opts:
         o["split"] = int(opts["split"])
+    if "tile_join" in opts:
+        o["tile_join"] = int(opts["tile_join"])
     o["stream_rows"] = max(0, o["stream_rows"])     # negative: no single-wave items
     ts_q, ts_c, gamma, rb = o["ts_q"], o["ts_c"], o["gamma"], o["rb"]
     parent = [int(x) for x in parent]
@@ -246,8 +251,11 @@ def build_plan(parent, node_len, node_page_ptr, node_page_ids, page_size, qpl,
                            rows=len(qs) * g))
 
     # ---- P6 / P7: item class, row blocks and KV chunks
+    has_wg = any(G["rows"] > o["stream_rows"] for G in groups)
     for G in groups:
-        G["cls"] = 0 if G["rows"] <= o["stream_rows"] else 1   # 0 = stream (one wave), 1 = workgroup
+        # 0 = stream (one wave), 1 = workgroup
+        single = G["rows"] <= o["stream_rows"] and not (o["tile_join"] and has_wg and G["rows"] >= TILE_ROWS)
+        G["cls"] = 0 if single else 1
         if G["cls"] == 0:
             G["nblocks"], G["rb"] = 1, G["rows"]
         else:   # balanced blocks of at most rb rows, 16-aligned when rb is
@@ -344,7 +352,8 @@ def build_plan(parent, node_len, node_page_ptr, node_page_ids, page_size, qpl,
     params = [FORMAT_VERSION, n, n_q, qpl, n_qheads, n_kvheads, head_dim, page_size,
               ts_q, ts_c, gamma, rb, o["waves"], o["floor_f"], o["ncu"], o["split"],
               1 if force_edges is not None else 0, CHUNK_ALIGN, len(groups), len(chunks),
-              len(items), n_slots, c_glob, len(runs), o["stream_rows"], n_stream, o["split_align"]]
+              len(items), n_slots, c_glob, len(runs), o["stream_rows"], n_stream, o["split_align"],
+              1 if o["tile_join"] else 0]
     gq, gv, gt = [], [], []
     for G in groups:
         gt.append([G["node"], G["top"], G["kv_len"], len(G["qs"]), len(gq), G["chunk_ptr"],

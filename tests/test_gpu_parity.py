@@ -81,7 +81,7 @@ def test_plan_invariance(k):
     variants = [dict(force_edges=[0] * n), dict(force_edges=[1] * n),
                 dict(force_edges=rng.integers(0, 2, n).tolist()), dict(split=False),
                 dict(ncu=1024, ts_c=16, split_align=16), dict(rb=32, floor_f=1), dict(waves=1, ncu=64),
-                dict(waves=8, split_align=64)]
+                dict(waves=8, split_align=64), dict(tile_join=False)]
     for kw in variants:
         got = _run(inst, dev, **kw)
         _check(got[rows], ref[rows], f"config {k} {kw if 'force_edges' not in kw else 'forced'}")

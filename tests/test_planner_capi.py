@@ -40,6 +40,7 @@ def test_workload_plans_variants_bit_exact(k):
     _compare(inst, force_edges=[0] * inst.n_nodes)
     _compare(inst, force_edges=[1] * inst.n_nodes)
     _compare(inst, ts_c=128, gamma=8, rb=64, waves=2, floor_f=8, ncu=304)
+    _compare(inst, tile_join=0)
 
 
 def test_random_trees_bit_exact():
@@ -56,7 +57,8 @@ def test_random_trees_bit_exact():
             kw.update(split=0, ts_q=4, gamma=int(rng.integers(1, 200)))
         elif r == 4:
             kw.update(waves=int(rng.integers(1, 8)), floor_f=int(rng.integers(1, 16)), ncu=16,
-                      split_align=int(rng.choice([16, 32, 48, 128])))
+                      split_align=int(rng.choice([16, 32, 48, 128])), tile_join=int(rng.integers(0, 2)),
+                      stream_rows=int(rng.choice([16, 32, 64])))
         _compare(inst, **kw)
 
 

@@ -126,13 +126,16 @@ def check_invariants(inst, plan):
     total = sum(int(G[3]) * g * int(G[6]) for G in groups)
     assert len(seen) == total
     # (4b) classes: single-wave items are groups of at most stream_rows rows, in
-    # one row block; workgroup items come first in launch order
-    srows = int(P[24])
+    # one row block, except (tile_join) groups of a full 16-row tile in a plan
+    # that has workgroup items; workgroup items come first in launch order
+    srows, join = int(P[24]), int(P[27])
     cls = plan["items"][:, 4]
     assert (np.diff(cls) <= 0).all() and int(P[25]) == int((cls == 0).sum())
+    has_wg = any(int(G[3]) * g > srows for G in groups)
     for gi_, r0, nr, ci, c in plan["items"]:
         rows_g = int(groups[gi_][3]) * g
-        assert c == (0 if rows_g <= srows else 1)
+        single = rows_g <= srows and not (join and has_wg and rows_g >= 16)
+        assert c == (0 if single else 1)
         if c == 0:
             assert r0 == 0 and nr == rows_g
     # (5) slots are a bijection onto (group, chunk, query-in-group)

@@ -32,7 +32,8 @@ class Plan:
     def __init__(self, parent, node_kv_len, node_page_ptr, node_page_ids, page_size,
                  queries_per_leaf, n_qheads, n_kvheads, head_dim, *, force_edges=None,
                  host_only=False, scale=0.0, poison_workspace=False, ts_q=0, ts_c=0, gamma=0,
-                 rb=0, waves=0, floor_f=0, ncu=0, split=True, stream_rows=0, split_align=0):
+                 rb=0, waves=0, floor_f=0, ncu=0, split=True, stream_rows=0, split_align=0,
+                 tile_join=True):
         L = lib()
         self._handle = ctypes.c_void_p()
         par, par_p = _i32(parent)
@@ -46,7 +47,8 @@ class Plan:
         opts = PlanOpts(ts_q=ts_q, ts_c=ts_c, gamma=gamma, rb=rb, waves=waves, floor_f=floor_f,
                         ncu=ncu, no_split=0 if split else 1, host_only=1 if host_only else 0,
                         scale=float(scale), poison_workspace=1 if poison_workspace else 0,
-                        stream_rows=int(stream_rows), split_align=int(split_align))
+                        stream_rows=int(stream_rows), split_align=int(split_align),
+                        no_tile_join=0 if tile_join else 1)
         self._force = None
         if force_edges is not None:
             fe = np.ascontiguousarray(np.asarray(force_edges), dtype=np.int8)

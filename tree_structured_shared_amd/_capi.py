@@ -32,7 +32,7 @@ class PlanOpts(ctypes.Structure):
         ("force_edges", ctypes.POINTER(ctypes.c_int8)), ("host_only", ctypes.c_int32),
         ("scale", ctypes.c_float), ("poison_workspace", ctypes.c_int32),
         ("stream_rows", ctypes.c_int32),
-        ("split_align", ctypes.c_int32),
+        ("split_align", ctypes.c_int32), ("no_tile_join", ctypes.c_int32),
     ]
 
 

@@ -368,6 +368,7 @@ ta_status tree_attn_plan(const int32_t* parent, int32_t n_nodes, const int32_t* 
       if (opts->ncu) pp.ncu = opts->ncu;
       if (opts->stream_rows) pp.stream_rows = opts->stream_rows < 0 ? 0 : opts->stream_rows;
       if (opts->split_align) pp.split_align = opts->split_align;
+      pp.tile_join = opts->no_tile_join ? 0 : 1;
     }
     int device = -1;
     if (!host_only) {

@@ -16,9 +16,11 @@
 //  P5  one group per virtual node with queries left (DeFT notes, KV-guided
 //      split: a node's KV grouped with every query that shares it).
 //  P6  item class and row blocks: a group with at most stream_rows rows is
-//      one single-wave stream block; a larger one is cut into balanced
-//      workgroup blocks of at most rb rows (16-aligned when rb is). Row r =
-//      (query r / g, q-head r % g).
+//      one single-wave stream block (unless tile_join and the plan has
+//      workgroup items and the group fills a 16-row tile: then it joins
+//      them, so a launch holds one item class where the rows allow); a
+//      larger one is cut into balanced workgroup blocks of at most rb rows
+//      (16-aligned when rb is). Row r = (query r / g, q-head r % g).
 //  P7  long-context split (FastTree review, section 3.3): a global chunk
 //      length sized so the launch gives about ncu * waves busy waves (a
 //      workgroup block counts as kBlockWaveWeight3 / 3 waves: its four waves
@@ -247,8 +249,15 @@ int plan_init(const int32_t* parent, int32_t n, const int32_t* node_len,
     }
     std::reverse(G.seg.begin(), G.seg.end());
     G.rows = int32_t(G.qs.size()) * S.g;
-    // ---- P6 item class and row blocks
-    G.cls = G.rows <= p.stream_rows ? 0 : 1;
+    group_of[v] = int32_t(S.groups.size());
+    S.groups.push_back(std::move(G));
+  }
+  // ---- P6 item class and row blocks
+  bool has_wg = false;
+  for (const PlanGroup& G : S.groups) has_wg = has_wg || G.rows > p.stream_rows;
+  for (PlanGroup& G : S.groups) {
+    const bool single = G.rows <= p.stream_rows && !(p.tile_join && has_wg && G.rows >= kTileRows);
+    G.cls = single ? 0 : 1;
     if (G.cls == 0) {
       G.nblocks = 1;
       G.rb = G.rows;
@@ -257,8 +266,6 @@ int plan_init(const int32_t* parent, int32_t n, const int32_t* node_len,
       G.rb = int32_t(align_up(cdiv(G.rows, nb), p.rb % 16 == 0 ? 16 : 1));
       G.nblocks = int32_t(cdiv(G.rows, G.rb));
     }
-    group_of[v] = int32_t(S.groups.size());
-    S.groups.push_back(std::move(G));
   }
 
   // ---- P9 structure: the groups each leaf's queries read, root side first
@@ -422,7 +429,7 @@ void plan_layout(PlanState& S, PlanTables& T) {
               p.ts_q, p.ts_c, p.gamma, p.rb, p.waves, p.floor_f, p.ncu, p.split ? 1 : 0,
               S.edges_mode, kChunkAlign, int32_t(S.groups.size()), n_chunks,
               int32_t(items.size()), n_slots, int32_t(c_glob), int32_t(n_runs),
-              p.stream_rows, n_stream, p.split_align};
+              p.stream_rows, n_stream, p.split_align, p.tile_join ? 1 : 0};
   T.edges = S.f;
   T.nq = S.nq;
   T.lcum.resize(size_t(n));

@@ -13,14 +13,16 @@ struct PlanParams {
   int32_t split_align = 128;  // chunk lengths of the split are multiples of this
   int32_t split = 1;
   int32_t stream_rows = 16;  // groups with at most this many rows run as one-wave items
+  int32_t tile_join = 1;     // ... except groups of a full 16-row tile when the plan has workgroup items
   const int8_t* force_edges = nullptr;
 };
 
-constexpr int32_t kFormatVersion = 3;
+constexpr int32_t kFormatVersion = 4;
+constexpr int32_t kTileRows = 16;       // rows of one MFMA row tile
 constexpr int64_t kBlockWaveWeight3 = 8; // split rule: a workgroup block counts as 8/3 busy waves
 constexpr int32_t kChunkAlign = 16;     // chunk lengths are multiples of the MFMA token block
 constexpr int64_t kItemFixedCost = 256; // per-item cost proxy in row units (longest-first order)
-constexpr int32_t kParamsLen = 27;
+constexpr int32_t kParamsLen = 28;
 // Page-table words after each group's segment (and its slack) that repeat the
 // segment's last token: the kernels may read a few tiles of words past a
 // segment's end unconditionally, and every word they can reach names a token
