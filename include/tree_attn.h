@@ -69,7 +69,8 @@ typedef struct {
   float scale;               /* softmax scale; 0 = 1/sqrt(head_dim) */
   int32_t poison_workspace;  /* 1 = fill the workspace with NaN before every decode (testing) */
   int32_t stream_rows;       /* groups with at most this many rows (query x q-head-in-group)
-                                run as single-wave items (default 16; -1 = none) */
+                                run as single-wave items, which compute one 16-row tile
+                                (1..16, default 16; -1 = none; above 16: TA_EINVAL) */
   int32_t split_align;       /* the split's chunk length is a multiple of this many tokens
                                 (a multiple of 16; default 128: four 32-token tiles) */
   int32_t no_tile_join;      /* 1 = groups of 16 or more rows stay single-wave items (when

@@ -127,6 +127,8 @@ def build_plan(parent, node_len, node_page_ptr, node_page_ids, page_size, qpl,
         raise PlanError("EUNSUPPORTED: head_dim")
     if not (1 <= page_size <= 256):
         raise PlanError("EINVAL: page_size")
+    if o["stream_rows"] > TILE_ROWS:   # a single-wave item computes one 16-row tile
+        raise PlanError("EINVAL: stream_rows")
     roots = [v for v in range(n) if parent[v] == -1]
     if len(roots) != 1:
         raise PlanError("EINVAL: need exactly one root")

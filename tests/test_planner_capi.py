@@ -58,7 +58,7 @@ def test_random_trees_bit_exact():
         elif r == 4:
             kw.update(waves=int(rng.integers(1, 8)), floor_f=int(rng.integers(1, 16)), ncu=16,
                       split_align=int(rng.choice([16, 32, 48, 128])), tile_join=int(rng.integers(0, 2)),
-                      stream_rows=int(rng.choice([16, 32, 64])))
+                      stream_rows=int(rng.choice([4, 8, 16])))
         _compare(inst, **kw)
 
 
@@ -103,6 +103,7 @@ def _plan_raw(parent, lens, ptr, ids, ps=16, qpl=1, hq=4, h=4, d=128, host_only=
     (dict(ids=[0, -3]), _capi.TA_EINVAL),                   # negative page id
     (dict(ps=0), _capi.TA_EINVAL),                          # page size
     (dict(split_align=24), _capi.TA_EINVAL),                # split alignment not a multiple of 16
+    (dict(stream_rows=17), _capi.TA_EINVAL),                # a single-wave item holds one 16-row tile
     (dict(waves=-1), _capi.TA_EINVAL),                      # negative option
 ])
 def test_plan_error_codes(case, status):

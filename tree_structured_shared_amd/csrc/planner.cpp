@@ -99,7 +99,7 @@ int plan_init(const int32_t* parent, int32_t n, const int32_t* node_len,
   if (page_size < 1 || page_size > 256)
     return fail(err, EINVAL_, "tree_attn_plan: page_size must be in 1..256");
   if (p.ts_q < 1 || p.ts_c < 1 || p.gamma < 0 || p.rb < 1 || p.waves < 1 || p.floor_f < 0 ||
-      p.ncu < 1 || p.stream_rows < 0 || p.split_align < 16 || p.split_align % 16)
+      p.ncu < 1 || p.stream_rows < 0 || p.stream_rows > kTileRows || p.split_align < 16 || p.split_align % 16)
     return fail(err, EINVAL_, "tree_attn_plan: invalid option value");
   int32_t root = -1;
   for (int32_t v = 0; v < n; ++v) {
