@@ -165,25 +165,32 @@ def _decode_loop(args, inst, dev):
     synchronisation in between. Reports wall time per step, host time per
     extend, the same decodes without growth, and the host time of planning
     the grown tree from scratch (what each step would cost without reuse).
-    K/V of the new tokens is left at zero: this mode times, it does not check."""
+    Each step first writes the new tokens' K/V into the pools with
+    tree_attn_kv_append (fixed rows: this mode times, it does not check)."""
     import numpy as np
     import torch
-    from tree_structured_shared_amd import Plan
+    from tree_structured_shared_amd import Plan, kv_append
     K, W = args.steps, args.warmup
     ps, qpl = inst.page_size, inst.qpl
     has_child = np.zeros(inst.n_nodes, bool)
     has_child[inst.parent[inst.parent >= 0]] = True
     leaves = np.flatnonzero(~has_child)
     lens = inst.node_len.astype(np.int64).copy()
-    next_page, sched = inst.n_pages, []
+    node_pages = [list(inst.node_page_ids[inst.node_page_ptr[v]:inst.node_page_ptr[v + 1]]) for v in leaves]
+    next_page, sched, dsts = inst.n_pages, [], []
     for _ in range(W + K):
-        pages = []
-        for v in leaves:
+        pages, locs = [], []
+        for x, v in enumerate(leaves):
             grow = -(-(lens[v] + qpl) // ps) - (-(-lens[v] // ps))
-            pages += list(range(next_page, next_page + grow))
+            fresh = list(range(next_page, next_page + grow))
+            pages += fresh
+            node_pages[x] += fresh
             next_page += grow
+            for t in range(int(lens[v]), int(lens[v]) + qpl):
+                locs.append((int(node_pages[x][t // ps]) << 8) | (t % ps))
             lens[v] += qpl
         sched.append(np.asarray(pages, np.int32))
+        dsts.append(torch.tensor(locs, dtype=torch.int32, device=dev))
     shape = (next_page,) + tuple(inst.k_pool.shape[1:])
     k = torch.zeros(shape, dtype=inst.dtype, device=dev)
     v = torch.zeros(shape, dtype=inst.dtype, device=dev)
@@ -191,11 +198,15 @@ def _decode_loop(args, inst, dev):
     v[:inst.n_pages].copy_(inst.v_pool)
     q = inst.q.to(dev)
     out = torch.empty((inst.n_queries, inst.n_qheads, inst.head_dim), dtype=torch.float32, device=dev)
+    new_rows = len(leaves) * qpl
+    k_new = torch.randn((new_rows, inst.n_kvheads, inst.head_dim), device=dev).to(inst.dtype)
+    v_new = torch.randn((new_rows, inst.n_kvheads, inst.head_dim), device=dev).to(inst.dtype)
     plan = Plan.for_instance(inst)
     stream = torch.cuda.current_stream(dev).cuda_stream
     call = plan.launcher(q, k, v, out, stream)
     add = np.full(len(leaves), qpl, np.int32)
     for s in range(W):
+        kv_append(k, v, k_new, v_new, dsts[s], stream)
         plan.extend(add, sched[s], stream)
         call()
     torch.cuda.synchronize()
@@ -203,18 +214,19 @@ def _decode_loop(args, inst, dev):
     gc.disable()
     t0 = time.perf_counter()
     for s in range(W, W + K):
+        kv_append(k, v, k_new, v_new, dsts[s], stream)
         a = time.perf_counter()
         relaunches += int(plan.extend(add, sched[s], stream))
         t_ext.append(time.perf_counter() - a)
         call()
     torch.cuda.synchronize()
     loop_us = (time.perf_counter() - t0) * 1e6 / K
-    gc.enable()
     t0 = time.perf_counter()
     for s in range(K):
         call()
     torch.cuda.synchronize()
     static_us = (time.perf_counter() - t0) * 1e6 / K
+    gc.enable()
     import dataclasses
     g_inst = dataclasses.replace(inst, node_len=lens.astype(np.int32), q=None, k_pool=None, v_pool=None)
     ptr = np.zeros(inst.n_nodes + 1, np.int32)
@@ -228,7 +240,8 @@ def _decode_loop(args, inst, dev):
         t_fresh.append(time.perf_counter() - a)
     P = plan.export("params")
     print(json.dumps({"decode_loop": inst.name, "steps": K, "warmup": W, "tokens_per_leaf_per_step": qpl,
-                      "us_per_step_with_extend": round(loop_us, 2), "us_per_step_no_growth": round(static_us, 2),
+                      "us_per_step_append_extend_decode": round(loop_us, 2),
+                      "us_per_step_no_growth": round(static_us, 2),
                       "extend_host_us_median": round(statistics.median(t_ext) * 1e6, 2),
                       "extend_host_us_p90": round(sorted(t_ext)[int(0.9 * (len(t_ext) - 1))] * 1e6, 2),
                       "extend_host_us_max": round(max(t_ext) * 1e6, 2),

@@ -147,6 +147,18 @@ ta_status tree_attn_decode(const void* q, ta_dtype q_dtype, const ta_paged_kv* k
 ta_status tree_attn_plan_extend(ta_plan* plan, const int32_t* leaf_add, const int32_t* new_pages,
                                 int64_t n_new_pages, void* hip_stream, int32_t* relaunch);
 
+/* KV append, the step before a decode (the new tokens' K and V into the
+ * paged pools). Token r's rows k_new[r, n_kvheads, head_dim] and
+ * v_new[r, n_kvheads, head_dim] (device, contiguous, kv->dtype) are written to
+ * page dst[r] >> 8, slot dst[r] & 255 of the pools (dst: device int32
+ * [n_tokens], the encoding of TA_T_SEG_TOK). Asynchronous on hip_stream. A
+ * destination outside the pools (page >= kv->n_pages, slot >= page_size, or a
+ * negative word) is skipped, never written. Two tokens with the same
+ * destination race. TA_EINVAL / TA_EUNSUPPORTED for bad sizes, strides or
+ * alignment (the rules of tree_attn_decode); n_tokens == 0 does nothing. */
+ta_status tree_attn_kv_append(const ta_paged_kv* kv, const void* k_new, const void* v_new, int64_t n_tokens,
+                              int32_t n_kvheads, int32_t head_dim, const int32_t* dst, void* hip_stream);
+
 /* Plan sizes. Any output pointer may be NULL. */
 ta_status tree_attn_plan_info(const ta_plan* plan, int32_t* n_queries, int64_t* workspace_bytes,
                               int32_t* n_items);

@@ -123,3 +123,69 @@ def test_extend_graph_replay():
         _check(replayed, ta.decode_instance(inst), f"graph step {step} relaunch {relaunch}")
     assert replays >= 1, "no extend kept the captured graph valid"
     plan.close()
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.bfloat16, 64), (torch.float32, 128)])
+def test_kv_append_scatter(dtype, d):
+    """Rows land bit for bit where the page-table words say; destinations
+    outside the pool are skipped."""
+    from tree_structured_shared_amd import kv_append
+    g = torch.Generator().manual_seed(d)
+    n_pages, ps, h, n = 40, 16, 4, 300
+    k_pool = torch.randn((n_pages, ps, h, d), generator=g).to(dtype)
+    v_pool = torch.randn((n_pages, ps, h, d), generator=g).to(dtype)
+    k_new = torch.randn((n, h, d), generator=g).to(dtype)
+    v_new = torch.randn((n, h, d), generator=g).to(dtype)
+    cells = torch.randperm(n_pages * ps, generator=g)[:n]
+    page, slot = cells // ps, cells % ps
+    dst = (page << 8) | slot
+    dst[::37] = (n_pages + 3) << 8          # past the pool: skipped
+    dst[5] = (2 << 8) | 200                 # slot past the page: skipped
+    dst[6] = -1                             # negative word: skipped
+    ok = (dst >= 0) & ((dst >> 8) < n_pages) & ((dst & 255) < ps)
+    want_k, want_v = k_pool.clone(), v_pool.clone()
+    want_k[page[ok], slot[ok]] = k_new[ok]
+    want_v[page[ok], slot[ok]] = v_new[ok]
+    kd, vd = k_pool.cuda(), v_pool.cuda()
+    kv_append(kd, vd, k_new.cuda(), v_new.cuda(), dst.to(torch.int32).cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(kd.cpu(), want_k) and torch.equal(vd.cpu(), want_v)
+
+
+def test_decode_loop_append_extend_decode():
+    """A decode loop through the library only: the new tokens' K/V go in with
+    kv_append, the plan grows with extend, the decode matches the oracle on
+    the grown tree; the device pools equal the grown instance's pools."""
+    from tree_structured_shared_amd import kv_append
+    inst = _small_tree(torch.bfloat16, 2)
+    spare = 64
+    kd = torch.zeros((inst.n_pages + spare,) + tuple(inst.k_pool.shape[1:]), dtype=inst.dtype, device="cuda")
+    vd = torch.full(kd.shape, synth.CANARY_V, dtype=torch.float32, device="cuda").to(inst.dtype)
+    kd[:inst.n_pages].copy_(inst.k_pool)
+    vd[:inst.n_pages].copy_(inst.v_pool)
+    plan = Plan.for_instance(inst, poison_workspace=True)
+    has_child = np.zeros(inst.n_nodes, bool)
+    has_child[inst.parent[inst.parent >= 0]] = True
+    leaves = np.flatnonzero(~has_child)
+    for step in range(5):
+        add = np.full(inst.n_leaves, inst.qpl) + (step == 2) * 30
+        grown, new_pages = synth.grow_leaves(inst, add, seed=900 + step)
+        assert grown.n_pages <= kd.shape[0]
+        # the new tokens, leaf-rank order, and where the grown tree puts them
+        locs, rows_k, rows_v = [], [], []
+        for v in leaves:
+            pages = grown.node_page_ids[grown.node_page_ptr[v]:grown.node_page_ptr[v + 1]]
+            for t in range(int(inst.node_len[v]), int(grown.node_len[v])):
+                pg, sl = int(pages[t // grown.page_size]), t % grown.page_size
+                locs.append((pg << 8) | sl)
+                rows_k.append(grown.k_pool[pg, sl])
+                rows_v.append(grown.v_pool[pg, sl])
+        kv_append(kd, vd, torch.stack(rows_k).cuda().contiguous(), torch.stack(rows_v).cuda().contiguous(),
+                  torch.tensor(locs, dtype=torch.int32, device="cuda"))
+        plan.extend(add, new_pages)
+        out = plan.decode(grown.q.cuda(), kd, vd)
+        _check(out, ta.decode_instance(grown), f"append+extend step {step}")
+        assert torch.equal(kd[:grown.n_pages].cpu(), grown.k_pool)
+        assert torch.equal(vd[:grown.n_pages].cpu(), grown.v_pool)
+        inst = grown
+    plan.close()

@@ -233,3 +233,18 @@ def test_graph_capture_replays():
         torch.cuda.synchronize()
         assert torch.equal(other, eager)
     plan.close()
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_prefill_of_new_nodes(dtype):
+    """Prefill of new nodes as tree attention: every token of a new leaf is a
+    query (queries_per_leaf = its length), causal inside the leaf, over the
+    shared ancestors (two new 256-token leaves under a 700-token prompt)."""
+    qpl = 256
+    par = [-1, 0, 1, 1]
+    lens = [700, 90, qpl, qpl]
+    inst = synth.make_tree(par, lens, page_size=16, qpl=qpl, n_qheads=16, n_kvheads=4, head_dim=128,
+                           dtype=dtype, seed=11)
+    synth.fill_tensors(inst, seed=12)
+    ref = ta.decode_instance(inst)
+    _check(_run(inst), ref, f"prefill {dtype}")

@@ -142,3 +142,22 @@ def test_python_wrapper_raises():
     p = Plan([-1, 0], [4, 4], [0, 1, 2], [0, 1], 16, 1, 4, 4, 128, host_only=True)
     with pytest.raises(TreeAttnError):
         p.decode(None, None, None)
+
+
+def test_kv_append_argument_errors():
+    """Argument checks of tree_attn_kv_append run before any HIP call."""
+    L = _capi.lib()
+    kv = _capi.PagedKV(k=256, v=512, dtype=_capi.TA_BF16, page_size=16, n_pages=4, stride_page=16 * 4 * 128,
+                       stride_token=4 * 128, stride_head=128)
+    def call(kvp, n=8, h=4, d=128, knew=1024, vnew=2048, dst=4096):
+        return L.tree_attn_kv_append(kvp, knew, vnew, n, h, d, dst, None)
+    assert call(None) == _capi.TA_EINVAL                                   # no pools
+    assert call(ctypes.byref(kv), n=-1) == _capi.TA_EINVAL                 # negative count
+    assert call(ctypes.byref(kv), knew=None) == _capi.TA_EINVAL            # missing rows
+    assert call(ctypes.byref(kv), d=96) == _capi.TA_EUNSUPPORTED           # head_dim
+    assert call(ctypes.byref(kv), h=0) == _capi.TA_EINVAL                  # kv-heads
+    assert call(ctypes.byref(kv), knew=1032) == _capi.TA_EINVAL            # misaligned rows
+    bad = _capi.PagedKV(k=256, v=512, dtype=_capi.TA_BF16, page_size=16, n_pages=4, stride_page=16 * 4 * 128,
+                        stride_token=4 * 128, stride_head=100)
+    assert call(ctypes.byref(bad)) == _capi.TA_EINVAL                      # stride not 16-byte
+    assert call(ctypes.byref(kv), n=0) == _capi.TA_OK                      # nothing to do

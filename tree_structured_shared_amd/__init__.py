@@ -18,12 +18,41 @@ import numpy as np
 from ._capi import (TA_BF16, TA_F32, TABLE_COLS, TABLE_IDS, PagedKV, PlanOpts, TreeAttnError,
                     check, lib)
 
-__all__ = ["Plan", "TreeAttnError", "TABLE_IDS"]
+__all__ = ["Plan", "TreeAttnError", "TABLE_IDS", "kv_append"]
 
 
 def _i32(a):
     arr = np.ascontiguousarray(np.asarray(a), dtype=np.int32)
     return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def kv_append(k_pool, v_pool, k_new, v_new, dst, stream=None):
+    """Write the new tokens' K/V rows into the paged pools
+    (tree_attn_kv_append): token r's rows k_new[r] / v_new[r]
+    ([n_kvheads, head_dim]) go to page dst[r] >> 8, slot dst[r] & 255; dst is a
+    device int32 tensor. Destinations outside the pools are skipped."""
+    import torch
+    dt = {torch.float32: TA_F32, torch.bfloat16: TA_BF16}.get(k_pool.dtype)
+    if dt is None:
+        raise TreeAttnError(4, f"unsupported dtype {k_pool.dtype}")
+    if k_pool.dim() != 4 or k_pool.shape != v_pool.shape or k_pool.stride() != v_pool.stride():
+        raise TreeAttnError(1, "pools must be [n_pages, page_size, n_kvheads, head_dim] with equal strides")
+    n, h, d = k_new.shape[0], k_pool.shape[2], k_pool.shape[3]
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if tuple(t.shape) != (n, h, d) or t.dtype != k_pool.dtype or not t.is_contiguous() or not t.is_cuda:
+            raise TreeAttnError(1, f"{name} must be a contiguous device [n_tokens, {h}, {d}] {k_pool.dtype} tensor")
+    if (dst.dtype != torch.int32 or tuple(dst.shape) != (n,) or not dst.is_contiguous() or not dst.is_cuda):
+        raise TreeAttnError(1, "dst must be a contiguous device int32 [n_tokens] tensor")
+    if k_pool.stride(3) != 1:
+        raise TreeAttnError(1, "head_dim must be contiguous in the pools")
+    kv = PagedKV(k=k_pool.data_ptr(), v=v_pool.data_ptr(), dtype=dt, page_size=k_pool.shape[1],
+                 n_pages=k_pool.shape[0], stride_page=k_pool.stride(0), stride_token=k_pool.stride(1),
+                 stride_head=k_pool.stride(2))
+    if stream is None:
+        stream = torch.cuda.current_stream(k_pool.device).cuda_stream
+    check(lib().tree_attn_kv_append(ctypes.byref(kv), ctypes.c_void_p(k_new.data_ptr()),
+                                    ctypes.c_void_p(v_new.data_ptr()), int(n), int(h), int(d),
+                                    ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(stream)))
 
 
 class Plan:

@@ -556,6 +556,44 @@ ta_status tree_attn_decode(const void* q, ta_dtype q_dtype, const ta_paged_kv* k
   return TA_OK;
 }
 
+ta_status tree_attn_kv_append(const ta_paged_kv* kv, const void* k_new, const void* v_new, int64_t n_tokens,
+                              int32_t n_kvheads, int32_t head_dim, const int32_t* dst, void* hip_stream) {
+  g_err.clear();
+  if (!kv || !kv->k || !kv->v) return set_err(TA_EINVAL, "tree_attn_kv_append: NULL pool");
+  if (n_tokens < 0) return set_err(TA_EINVAL, "tree_attn_kv_append: negative token count");
+  if (n_tokens > 0 && (!k_new || !v_new || !dst)) return set_err(TA_EINVAL, "tree_attn_kv_append: NULL argument");
+  if (kv->dtype != TA_F32 && kv->dtype != TA_BF16)
+    return set_err(TA_EUNSUPPORTED, "tree_attn_kv_append: dtype must be TA_F32 or TA_BF16");
+  if (head_dim != 64 && head_dim != 128) return set_err(TA_EUNSUPPORTED, "tree_attn_kv_append: head_dim must be 64 or 128");
+  if (n_kvheads < 1 || kv->page_size < 1 || kv->page_size > 256 || kv->n_pages < 1)
+    return set_err(TA_EINVAL, "tree_attn_kv_append: bad n_kvheads, page_size or n_pages");
+  const int64_t es = kv->dtype == TA_BF16 ? 2 : 4, vec = 16 / es;
+  if (kv->stride_page <= 0 || kv->stride_token <= 0 || kv->stride_head <= 0 ||
+      kv->stride_page % vec || kv->stride_token % vec || kv->stride_head % vec)
+    return set_err(TA_EINVAL, "tree_attn_kv_append: strides must be positive multiples of 16 bytes");
+  if ((reinterpret_cast<uintptr_t>(kv->k) | reinterpret_cast<uintptr_t>(kv->v) |
+       reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15)
+    return set_err(TA_EINVAL, "tree_attn_kv_append: pointers must be 16-byte aligned");
+  if (n_tokens == 0) return TA_OK;
+  ta::AppendArgs a{};
+  a.k_new = static_cast<const char*>(k_new);
+  a.v_new = static_cast<const char*>(v_new);
+  a.k = static_cast<char*>(const_cast<void*>(kv->k));
+  a.v = static_cast<char*>(const_cast<void*>(kv->v));
+  a.dst = dst;
+  a.n_tokens = n_tokens;
+  a.n_pages = kv->n_pages;
+  a.sp_bytes = kv->stride_page * es;
+  a.st_bytes = kv->stride_token * es;
+  a.sh_bytes = kv->stride_head * es;
+  a.n_kvheads = n_kvheads;
+  a.row_bytes = int32_t(head_dim * es);
+  a.page_size = kv->page_size;
+  const hipError_t e = ta::launch_append(a, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return hip_err(e, "tree_attn_kv_append: launch");
+  return TA_OK;
+}
+
 ta_status tree_attn_plan_info(const ta_plan* plan, int32_t* n_queries, int64_t* workspace_bytes,
                               int32_t* n_items) {
   g_err.clear();

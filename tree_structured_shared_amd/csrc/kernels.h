@@ -81,6 +81,22 @@ hipError_t launch_partial(const PartialArgs& a, int32_t n_block_items, int32_t n
                           int head_dim, hipStream_t s, KernelTimer t = {});
 hipError_t launch_reduce(const ReduceArgs& a, int head_dim, hipStream_t s, KernelTimer t = {});
 hipError_t launch_fill(float* p, int64_t n, float value, hipStream_t s);
+
+// KV append: token r's rows (n_kvheads x row_bytes, contiguous, r-major) of
+// k_new / v_new go to pool page dst[r] >> 8, slot dst[r] & 255; element
+// strides as in PartialArgs. Rows whose page is >= n_pages or whose slot is
+// >= page_size are skipped.
+struct AppendArgs {
+  const char* k_new;
+  const char* v_new;
+  char* k;
+  char* v;
+  const int32_t* dst;
+  int64_t n_tokens, n_pages;
+  int64_t sp_bytes, st_bytes, sh_bytes;  // page, token and head strides in bytes
+  int32_t n_kvheads, row_bytes, page_size;
+};
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 // Table update: stage holds n_desc descriptors (destination word, words,
 // source word in stage) followed by the words; each range is copied into
 // dst[0, dst_words). The host checks every range lies inside dst.

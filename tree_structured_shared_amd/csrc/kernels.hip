@@ -1052,6 +1052,28 @@ __global__ void scatter_kernel(int32_t* dst, int64_t dst_words, const int32_t* s
   }
 }
 
+// KV append: 16 lanes per 256-byte head row (16 bytes each), grid-stride over
+// (token, kv-head) rows; a destination outside the pool is skipped.
+__global__ void append_kernel(AppendArgs a) {
+  const int64_t rows = a.n_tokens * a.n_kvheads;
+  const int chunks = a.row_bytes >> 4;  // 16-byte pieces per head row
+  const int64_t step = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t x = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; x < rows * chunks; x += step) {
+    const int64_t row = x / chunks;
+    const int c = int(x - row * chunks);
+    const int64_t r = row / a.n_kvheads;
+    const int h = int(row - r * a.n_kvheads);
+    const int32_t loc = a.dst[r];
+    const int64_t page = loc >> 8;
+    const int slot = loc & 255;
+    if (loc < 0 || page >= a.n_pages || slot >= a.page_size) continue;
+    const int64_t src = row * a.row_bytes + 16 * c;
+    const int64_t off = page * a.sp_bytes + slot * a.st_bytes + h * a.sh_bytes + 16 * c;
+    *reinterpret_cast<u32x4*>(a.k + off) = *reinterpret_cast<const u32x4*>(a.k_new + src);
+    *reinterpret_cast<u32x4*>(a.v + off) = *reinterpret_cast<const u32x4*>(a.v_new + src);
+  }
+}
+
 __global__ void fill_kernel(float* p, int64_t n, float value) {
   for (int64_t x = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; x < n; x += int64_t(gridDim.x) * blockDim.x)
     p[x] = value;
@@ -1104,6 +1126,14 @@ hipError_t launch_scatter(int32_t* dst, int64_t dst_words, const int32_t* stage,
   if (n_desc <= 0) return hipSuccess;
   hipLaunchKernelGGL(scatter_kernel, dim3(unsigned(std::min(n_desc, 1024))), dim3(256), 0, s, dst, dst_words, stage,
                      n_desc);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
+  const int64_t work = a.n_tokens * a.n_kvheads * (a.row_bytes >> 4);
+  if (work <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((work + 255) / 256, 8192);
+  hipLaunchKernelGGL(append_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
