@@ -248,3 +248,38 @@ def test_prefill_of_new_nodes(dtype):
     synth.fill_tensors(inst, seed=12)
     ref = ta.decode_instance(inst)
     _check(_run(inst), ref, f"prefill {dtype}")
+
+
+def _strided_pools(inst, layout):
+    """The instance's pools in another layout, as [n_pages, page_size, H, d]
+    views with head_dim contiguous."""
+    if layout == "head_major":     # storage [pages, H, page_size, d]
+        mk = lambda p: p.permute(0, 2, 1, 3).contiguous().cuda().permute(0, 2, 1, 3)
+    else:                          # each page padded to 16 MiB: byte offsets past 32 bits' fast path
+        def mk(p):
+            n_pages, ps, h, d = p.shape
+            esz = p.element_size()
+            pad_tokens = max(ps, (16 << 20) // (h * d * esz))
+            big = torch.zeros((n_pages, pad_tokens, h, d), dtype=p.dtype, device="cuda")
+            big[:, :ps].copy_(p)
+            return big[:, :ps]
+    return mk(inst.k_pool), mk(inst.v_pool)
+
+
+@pytest.mark.parametrize("layout,dtype", [("head_major", torch.bfloat16), ("head_major", torch.float32),
+                                          ("padded_pages", torch.bfloat16)])
+def test_pool_layouts(layout, dtype):
+    """Pools in any layout with head_dim contiguous: head-major pages, and
+    pages 16 MiB apart (the kernels' 64-bit address path)."""
+    par = [-1, 0, 0, 1, 2, 2]
+    lens = [400, 50, 33, 20 + 16, 17, 64]
+    inst = synth.make_tree(par, lens, page_size=16, qpl=2, n_qheads=8, n_kvheads=2, head_dim=128, dtype=dtype,
+                           seed=21)
+    synth.fill_tensors(inst, seed=22)
+    ref = ta.decode_instance(inst)
+    k, v = _strided_pools(inst, layout)
+    plan = Plan.for_instance(inst, poison_workspace=True)
+    got = plan.decode(inst.q.cuda(), k, v)
+    torch.cuda.synchronize()
+    _check(got.cpu().numpy().astype(np.float64), ref, f"pools {layout} {dtype}")
+    plan.close()
