@@ -46,7 +46,6 @@ import numpy as np
 
 FORMAT_VERSION = 4
 TILE_ROWS = 16          # rows of one MFMA row tile
-WAVES_PER_WG = 4
 BLOCK_WAVE_WEIGHT3 = 8   # split rule: a workgroup block counts as 8/3 busy waves
 CHUNK_ALIGN = 16
 ITEM_FIXED_COST = 256

@@ -13,11 +13,17 @@
 // its row count (the review's multi-stage query tiling: small tiles near the
 // leaves, large ones near the root):
 //  * workgroup items (many rows): one workgroup per item x kv-head. bf16:
-//    the workgroup loads each K/V tile once into LDS (two stages, one
-//    barrier per tile) and wave w computes row tiles w and w+4 (128 rows per
-//    workgroup) from it. fp32: each wave runs the GEMV path on row pairs.
+//    the workgroup streams each K/V tile once into LDS with direct loads
+//    (kLdsStages stages, one barrier per tile) and wave w computes row tiles
+//    w and w+4 (128 rows per workgroup) from it. fp32: each wave runs the
+//    GEMV path on row pairs.
 //  * single-wave items (up to 16 rows): each wave is one item x kv-head and
 //    streams its chunk alone with two tiles in flight.
+// A plan holds one class where its rows allow (the planner's tile join), so
+// most launches are of one kind.
+//
+// kv append: the new tokens' K/V rows scattered into their pool pages (the
+// step before a decode).
 // Row arithmetic:
 //  * bf16: v_mfma_f32_16x16x32_bf16 on a transposed formulation, 16-row
 //    tiles (padded for fewer rows: the items are bound by their K/V stream).
