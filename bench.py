@@ -92,11 +92,18 @@ def _cpu_baseline(inst, budget_s=12.0, max_reps=20):
         oracle.decode_instance(inst)
         times.append(time.perf_counter() - t0)
     med = statistics.median(times)
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), cpu)
+    except OSError:
+        pass
     return {
         "value": round(inst.unique_kv_bytes / med / 1e9, 4),
         "unit": "GB/s",
         "us_per_step": round(med * 1e6, 1),
         "cores": int(cores),
+        "cpu": cpu,
         "kind": "oracle",
         "sample": f"{len(times)} full decode steps of the same tree (all {inst.n_queries} queries, "
                   f"fp64 numpy), median",
