@@ -126,8 +126,9 @@ ta_status tree_attn_decode(const void* q, ta_dtype q_dtype, const ta_paged_kv* k
  * last queries_per_leaf tokens again. Leaf of rank r (ascending node id) grows
  * by leaf_add[r] >= 0 tokens (leaf_add has one entry per leaf); the pages the
  * growth needs, ceil(new_len / page_size) - ceil(old_len / page_size) per
- * leaf, are taken in leaf-rank order from new_pages[n_new_pages] (device page
- * ids, [0, 2^23); the caller has written their K/V). The edge assignment and
+ * leaf, are taken in leaf-rank order from the host array
+ * new_pages[n_new_pages] (page ids of the pools, [0, 2^23); their K/V is
+ * written by the caller, e.g. with tree_attn_kv_append). The edge assignment and
  * so the context-query grouping are kept (FastTree review, section 3.2: the
  * grouping is a per-tree decision; call tree_attn_plan again to regroup); the
  * length-dependent steps (chunks, work items, slots, page table) are redone,
