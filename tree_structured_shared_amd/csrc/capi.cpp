@@ -39,7 +39,7 @@ struct ta_plan {
   int device = -1;
   // Device tables, one allocation of kRegions regions (word offsets / capacities):
   // work items, group query ids, visible prefixes, page table (guarded segments), slot CSR,
-  // slot positions.
+  // slot workspace indices (two words per slot).
   void* d_tables = nullptr;
   size_t reg_off[6] = {}, reg_cap[6] = {}, tables_words = 0;
   ta::WorkItem* d_items = nullptr;
@@ -117,8 +117,8 @@ inline size_t align64w(size_t words) { return (words + 63) & ~size_t(63); }  // 
 constexpr int kWordsPerItem = int(sizeof(ta::WorkItem) / 4);
 
 // Device forms of the plan's tables: work items in launch order and the
-// workspace position of every slot (query-major, so each query's partials
-// are contiguous in path order and the reduction needs no slot list).
+// workspace index of every slot (pair-major, so each (query, q-head)'s
+// partials are contiguous in path order and the reduction needs no slot list).
 void device_forms(ta_plan* p) {
   const ta::PlanTables& T = p->T;
   // visible tokens of each query over its whole path (sum over its groups)
@@ -146,8 +146,17 @@ void device_forms(ta_plan* p) {
     w.flags = min_vis < ta::kHiLoMinPath ? 1 : 0;
     p->h_items[x] = w;
   }
-  p->h_slot_pos.assign(T.q_slots.size(), 0);
-  for (size_t k = 0; k < T.q_slots.size(); ++k) p->h_slot_pos[T.q_slots[k]] = int32_t(k);
+  // per slot: workspace index of its q-head 0 and the q-head stride, pair-major
+  // (the slots of one (query, q-head) adjacent, so the reduction reads them in
+  // one run)
+  p->h_slot_pos.assign(2 * T.q_slots.size(), 0);
+  for (int32_t q = 0; q < T.n_queries; ++q) {
+    const int32_t s0 = T.q_slot_ptr[q], nsl = T.q_slot_ptr[q + 1] - s0;
+    for (int32_t k = s0; k < s0 + nsl; ++k) {
+      p->h_slot_pos[2 * size_t(T.q_slots[k])] = s0 * p->n_qheads + (k - s0);
+      p->h_slot_pos[2 * size_t(T.q_slots[k]) + 1] = nsl;
+    }
+  }
 }
 
 // Words each device region needs now.
@@ -158,7 +167,7 @@ void region_sizes(const ta_plan* p, size_t (&w)[6]) {
   w[2] = T.group_vis.size();
   w[3] = T.seg_tok.size();  // every segment ends in the planner's guard words
   w[4] = T.q_slot_ptr.size();
-  w[5] = T.q_slots.size();
+  w[5] = 2 * T.q_slots.size();
 }
 
 int64_t workspace_need(const ta_plan* p) {
@@ -203,6 +212,8 @@ ta_status ensure_workspace(ta_plan* p, bool headroom, bool* moved) {
 // no enqueued work reads the old tables.
 ta_status upload_full(ta_plan* p, bool headroom, bool* moved) {
   const ta::PlanTables& T = p->T;
+  if (int64_t(T.n_slots) * p->n_qheads >= int64_t(INT32_MAX))
+    return set_err(TA_EINVAL, "tree_attn_plan: partial slots x q-heads exceed 32-bit workspace indices");
   device_forms(p);
   p->h_vis = T.group_vis;
   p->h_q_slot_ptr = T.q_slot_ptr;
@@ -256,6 +267,8 @@ ta_status upload(ta_plan* p) {
 // and one copy, then one kernel scatters them, all in order on `s`.
 ta_status upload_incremental(ta_plan* p, hipStream_t s) {
   const ta::PlanTables& T = p->T;
+  if (int64_t(T.n_slots) * p->n_qheads >= int64_t(INT32_MAX))
+    return set_err(TA_EINVAL, "tree_attn_plan_extend: partial slots x q-heads exceed 32-bit workspace indices");
   std::vector<ta::WorkItem> old_items;
   old_items.swap(p->h_items);
   std::vector<int32_t> old_pos;

@@ -42,8 +42,10 @@ struct PartialArgs {
   const int32_t* group_qs;
   const int32_t* group_vis;
   const int32_t* seg_tok;  // (page << 8) | slot per segment token; each segment ends in guard words
-  const int32_t* slot_pos; // workspace position of each partial slot (query-major: query q's
-                           // slots, in path order, sit at [q_slot_ptr[q], q_slot_ptr[q + 1]))
+  const int32_t* slot_pos; // per partial slot two words: the workspace index of its q-head 0 and
+                           // the stride between q-heads. Pair-major: the slots of one (query q,
+                           // q-head h), in path order, are adjacent, at s0 * n_qheads + h * nsl +
+                           // [0, nsl) with s0 = q_slot_ptr[q], nsl = q_slot_ptr[q + 1] - s0
   const void* q;
   const void* k;
   const void* v;
@@ -59,7 +61,7 @@ struct PartialArgs {
 };
 
 struct ReduceArgs {
-  const int32_t* q_slot_ptr;  // query q's partials are at positions [q_slot_ptr[q], q_slot_ptr[q + 1])
+  const int32_t* q_slot_ptr;  // query q holds slots [q_slot_ptr[q], q_slot_ptr[q + 1]) (pair-major workspace)
   const float* o_part;
   const float* m_part;
   const float* l_part;

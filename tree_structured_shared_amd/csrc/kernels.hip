@@ -148,20 +148,22 @@ __device__ __forceinline__ float part_weight(float m, float M) {
 // ---------------------------------------------------------------------------
 // Rows of a work item. Row rr of the item is group row row0 + rr = (group
 // query qig, q-head-in-group hig); its partial goes to slot slot0 + qig, stored
-// at that slot's workspace position.
+// at that slot's workspace index for the row's q-head (pair-major layout).
 struct RowRef {
-  int gq, vis, slot, qh;
+  int gq, vis, qh;
+  int pbase, pstride;  // workspace index of this row's partial: pbase + qh * pstride
   bool ok;
 };
 
 __device__ __forceinline__ RowRef row_ref(const PartialArgs& a, const WorkItem& it, int h, int rr) {
-  RowRef r{0, 0, 0, 0, rr < it.nrows};
+  RowRef r{0, 0, 0, 0, 0, rr < it.nrows};
   if (r.ok) {
     const int grow = it.row0 + rr;
     const int qig = grow / a.g, hig = grow - qig * a.g;
     r.gq = a.group_qs[it.q_ptr + qig];
     r.vis = a.group_vis[it.q_ptr + qig];
-    r.slot = a.slot_pos[it.slot0 + qig];
+    r.pbase = a.slot_pos[2 * (it.slot0 + qig)];
+    r.pstride = a.slot_pos[2 * (it.slot0 + qig) + 1];
     r.qh = h * a.g + hig;
   }
   return r;
@@ -365,7 +367,7 @@ __device__ __forceinline__ void valu_write(const ValuState<T, D, R>& S, const Pa
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     if (!S.row[r].ok) continue;
-    const int64_t pi = int64_t(S.row[r].slot) * a.n_qheads + S.row[r].qh;
+    const int64_t pi = int64_t(S.row[r].pbase) + int64_t(S.row[r].qh) * S.row[r].pstride;
     float* op = a.o_part + pi * D + lane * EPL;
 #pragma unroll
     for (int k4 = 0; k4 < EPL / 4; ++k4)
@@ -645,7 +647,7 @@ __device__ __forceinline__ void mfma_write(MfmaState<D, NRTW>& S, const PartialA
     if (!S.on[k]) continue;
     const float l = sum4rows(S.l[k]);
     if (!S.row[k].ok) continue;
-    const int64_t pi = int64_t(S.row[k].slot) * a.n_qheads + S.row[k].qh;
+    const int64_t pi = int64_t(S.row[k].pbase) + int64_t(S.row[k].qh) * S.row[k].pstride;
     float* op = a.o_part + pi * D + 4 * j * DPL;
 #pragma unroll
     for (int x4 = 0; x4 < DPL; ++x4) {
@@ -995,7 +997,7 @@ __global__ __launch_bounds__(kBlock) void lse_reduce_kernel(ReduceArgs a) {
     int64_t pi[kReduceBatch];
 #pragma unroll
     for (int u = 0; u < kReduceBatch; ++u)
-      pi[u] = int64_t(min(b + kReduceGroups * u, s1 - 1)) * a.n_qheads + hq;
+      pi[u] = int64_t(s0) * a.n_qheads + int64_t(hq) * (s1 - s0) + (min(b + kReduceGroups * u, s1 - 1) - s0);
     float mv[kReduceBatch], lv[kReduceBatch];
     f32x4 ov[kReduceBatch][EPL / 4];
 #pragma unroll
