@@ -636,9 +636,11 @@ __device__ __forceinline__ void mfma_stream(MfmaState<D, NRTW>& S, const Partial
   }
 }
 
-// lane (i, j) holds O[row i][d = DPL * (4j + c) + db] = O[k][db][c]; l is
-// lane-partial (its 8 tokens per tile) and is summed over the row's 4 lanes
-template <int D, int NRTW>
+// lane (i, j) holds O[k][db][c] = O[row i][d], with d = DPL * (4j + c) + db
+// when V^T came from v_perm (single-wave items), d = 16 db + 4j + c when it
+// came from LDS transpose reads (workgroup items, TR); l is lane-partial (its
+// 8 tokens per tile) and is summed over the row's 4 lanes
+template <int D, int NRTW, bool TR = false>
 __device__ __forceinline__ void mfma_write(MfmaState<D, NRTW>& S, const PartialArgs& a) {
   constexpr int DPL = D / 16;
   const int j = (threadIdx.x & 63) >> 4;
@@ -648,16 +650,22 @@ __device__ __forceinline__ void mfma_write(MfmaState<D, NRTW>& S, const PartialA
     const float l = sum4rows(S.l[k]);
     if (!S.row[k].ok) continue;
     const int64_t pi = int64_t(S.row[k].pbase) + int64_t(S.row[k].qh) * S.row[k].pstride;
-    float* op = a.o_part + pi * D + 4 * j * DPL;
+    if constexpr (TR) {
+      float* op = a.o_part + pi * D + 4 * j;
 #pragma unroll
-    for (int x4 = 0; x4 < DPL; ++x4) {
-      f32x4 v;
+      for (int db = 0; db < DPL; ++db) *reinterpret_cast<f32x4*>(op + 16 * db) = S.O[k][db];
+    } else {
+      float* op = a.o_part + pi * D + 4 * j * DPL;
 #pragma unroll
-      for (int y = 0; y < 4; ++y) {
-        const int x = 4 * x4 + y;  // local offset = c * DPL + db
-        v[y] = S.O[k][x % DPL][x / DPL];
+      for (int x4 = 0; x4 < DPL; ++x4) {
+        f32x4 v;
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+          const int x = 4 * x4 + y;  // local offset = c * DPL + db
+          v[y] = S.O[k][x % DPL][x / DPL];
+        }
+        *reinterpret_cast<f32x4*>(op + 4 * x4) = v;
       }
-      *reinterpret_cast<f32x4*>(op + 4 * x4) = v;
     }
     if (j == 0) {
       a.m_part[pi] = S.m[k];
@@ -772,30 +780,56 @@ __device__ __forceinline__ void lds_tile(MfmaState<D, NRTW>& S, const char* stag
   bf16x8 pb[NACT], pl[NACT];
 #pragma unroll
   for (int k = 0; k < NACT; ++k) mfma_softmax<D, NRTW, HILO>(S, k, s0[k], s1[k], a, it, base, j, pb[k], pl[k]);
-  VSlice<DPL> vs[8];
+  if constexpr (NACT == 2) {
+    // V^T operands by LDS transpose reads: within each 16-lane group, lane L of
+    // a ds_read_b64_tr_b16 receives element k = the (L % 4)-th 16-bit value at
+    // the address of lane 4k + L / 4. Lane (i, j) points at token
+    // 16 r + 4 j + i / 4, d = 16 db + 4 (i % 4): it gets d = 16 db + i of tokens
+    // 16 r + 4 j + k, k = 0..3 -- with r = 0, 1 the token order tau(j, e) of P.
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4s lds_v4s;
+    typedef __attribute__((address_space(3))) char lds_b;
+    const lds_b* vstage = (const lds_b*)stage + L::PART;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int t = tau(j, e);
-    if constexpr (D == 128) {
-      vs[e].w = *reinterpret_cast<const u32x4*>(stage + L::off(1, t, i));
-    } else {
-      vs[e].w = *reinterpret_cast<const u32x2*>(stage + L::off(1, t, i >> 1) + (i & 1) * 8);
+    for (int db = 0; db < DPL; ++db) {
+      v4s half[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int t = 16 * r + 4 * j + (i >> 2);
+        const int c = 2 * db + ((i & 3) >> 1);
+        half[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4s*)(vstage + t * L::ROW + ((c ^ (t & (L::CH - 1))) << 4) + 8 * (i & 1)));
+      }
+      const bf16x8 vt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int k = 0; k < NACT; ++k) pv_update<D, NRTW, HILO>(S, k, db, vt, pb[k], pl[k]);
     }
-  }
-  // word w of a token's V slice holds d-blocks 2w (low halves) and 2w + 1
+  } else {  // one row tile: v_perm from two 16-byte reads per token is the shorter chain
+    VSlice<DPL> vs[8];
 #pragma unroll
-  for (int w = 0; w < DPL / 2; ++w) {
-    u32x4 lo, hi;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      lo[u] = __builtin_amdgcn_perm(vs[2 * u + 1].word(w), vs[2 * u].word(w), 0x05040100u);
-      hi[u] = __builtin_amdgcn_perm(vs[2 * u + 1].word(w), vs[2 * u].word(w), 0x07060302u);
+    for (int e = 0; e < 8; ++e) {
+      const int t = tau(j, e);
+      if constexpr (D == 128) {
+        vs[e].w = *reinterpret_cast<const u32x4*>(stage + L::off(1, t, i));
+      } else {
+        vs[e].w = *reinterpret_cast<const u32x2*>(stage + L::off(1, t, i >> 1) + (i & 1) * 8);
+      }
     }
-    const bf16x8 vlo = __builtin_bit_cast(bf16x8, lo), vhi = __builtin_bit_cast(bf16x8, hi);
+    // word w of a token's V slice holds d-blocks 2w (low halves) and 2w + 1
 #pragma unroll
-    for (int k = 0; k < NACT; ++k) {
-      pv_update<D, NRTW, HILO>(S, k, 2 * w, vlo, pb[k], pl[k]);
-      pv_update<D, NRTW, HILO>(S, k, 2 * w + 1, vhi, pb[k], pl[k]);
+    for (int w = 0; w < DPL / 2; ++w) {
+      u32x4 lo, hi;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        lo[u] = __builtin_amdgcn_perm(vs[2 * u + 1].word(w), vs[2 * u].word(w), 0x05040100u);
+        hi[u] = __builtin_amdgcn_perm(vs[2 * u + 1].word(w), vs[2 * u].word(w), 0x07060302u);
+      }
+      const bf16x8 vlo = __builtin_bit_cast(bf16x8, lo), vhi = __builtin_bit_cast(bf16x8, hi);
+#pragma unroll
+      for (int k = 0; k < NACT; ++k) {
+        pv_update<D, NRTW, HILO>(S, k, 2 * w, vlo, pb[k], pl[k]);
+        pv_update<D, NRTW, HILO>(S, k, 2 * w + 1, vhi, pb[k], pl[k]);
+      }
     }
   }
 }
@@ -909,7 +943,9 @@ __device__ __forceinline__ void block_lds_item(const PartialArgs& a, char* lds, 
     } else {
       lds_stream<D, FA, 0, false>(S, lds, a, it, h, i, j);
     }
-    mfma_write(S, a);
+    // waves with two row tiles built V^T by transpose reads (d = 16 db + 4j + c)
+    if (S.on[1]) mfma_write<D, kBlockRowTiles, true>(S, a);
+    else mfma_write<D, kBlockRowTiles, false>(S, a);
   }
 }
 
