@@ -419,6 +419,7 @@ struct MfmaState {
   static constexpr int KK = D / 32, DPL = D / 16;
   bf16x8 qf[NRTW][KK];
   f32x4 O[NRTW][DPL];
+  f32x4 L4[NRTW];  // l by MFMA (ones x P^T): every element of lane (i, j) is row i's l
   float m[NRTW], l[NRTW];
   RowRef row[NRTW];
   int vmin[NRTW];  // wave-uniform: smallest visible length over the tile's valid rows
@@ -439,6 +440,7 @@ __device__ __forceinline__ void mfma_init(MfmaState<D, NRTW>& S, const PartialAr
     S.row[k] = row_ref(a, it, h, on[k] ? rt[k] * 16 + i : it.nrows);
     S.m[k] = kMInit;
     S.l[k] = 0.0f;
+    S.L4[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int db = 0; db < DPL; ++db) S.O[k][db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -504,7 +506,9 @@ __device__ __forceinline__ void load_tile_kv(TileKV<D>& b, const TileSeg& sg, co
 // both bf16, so the P V product keeps ~16 mantissa bits of P; otherwise P is
 // rounded once to bf16 and l sums the rounded weights, so the output stays
 // an exact weighted average of V.
-template <int D, int NRTW, bool HILO>
+// With LMF the caller sums l on the matrix cores (ones x P^T into S.L4)
+// instead of here.
+template <int D, int NRTW, bool HILO, bool LMF = false>
 __device__ __forceinline__ void mfma_softmax(MfmaState<D, NRTW>& S, int k, const f32x4& s0, const f32x4& s1,
                                              const PartialArgs& a, const WorkItem& it, int base, int j,
                                              bf16x8& pb, bf16x8& pl) {
@@ -530,6 +534,7 @@ __device__ __forceinline__ void mfma_softmax(MfmaState<D, NRTW>& S, int k, const
   if (__builtin_amdgcn_ballot_w64(raise)) {  // rare after the first tiles
     const float al = raise ? fast_exp2(S.m[k] - mx) : 1.0f;
     S.l[k] *= al;
+    S.L4[k] *= al;
 #pragma unroll
     for (int db = 0; db < DPL; ++db) S.O[k][db] *= al;
     S.m[k] = raise ? mx : S.m[k];
@@ -541,17 +546,17 @@ __device__ __forceinline__ void mfma_softmax(MfmaState<D, NRTW>& S, int k, const
   for (int e = 0; e < 8; ++e) {
     p[e] = fast_exp2(__builtin_fmaf(sv[e], c, nm));
     pb[e] = __bf16(p[e]);
-    psum_r += float(pb[e]);
+    if constexpr (!LMF) psum_r += float(pb[e]);
   }
   if constexpr (HILO) {
     float psum = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      psum += p[e];
+      if constexpr (!LMF) psum += p[e];
       pl[e] = __bf16(p[e] - float(pb[e]));
     }
-    S.l[k] += psum;
-  } else {
+    if constexpr (!LMF) S.l[k] += psum;
+  } else if constexpr (!LMF) {
     S.l[k] += psum_r;
   }
 }
@@ -638,8 +643,9 @@ __device__ __forceinline__ void mfma_stream(MfmaState<D, NRTW>& S, const Partial
 
 // lane (i, j) holds O[k][db][c] = O[row i][d], with d = DPL * (4j + c) + db
 // when V^T came from v_perm (single-wave items), d = 16 db + 4j + c when it
-// came from LDS transpose reads (workgroup items, TR); l is lane-partial (its
-// 8 tokens per tile) and is summed over the row's 4 lanes
+// came from LDS transpose reads (workgroup items, TR). Without TR l is
+// lane-partial (its 8 tokens per tile) and is summed over the row's 4 lanes;
+// with TR it comes whole from the ones x P^T accumulator.
 template <int D, int NRTW, bool TR = false>
 __device__ __forceinline__ void mfma_write(MfmaState<D, NRTW>& S, const PartialArgs& a) {
   constexpr int DPL = D / 16;
@@ -647,7 +653,7 @@ __device__ __forceinline__ void mfma_write(MfmaState<D, NRTW>& S, const PartialA
 #pragma unroll
   for (int k = 0; k < NRTW; ++k) {
     if (!S.on[k]) continue;
-    const float l = sum4rows(S.l[k]);
+    const float l = TR ? S.L4[k][0] : sum4rows(S.l[k]);
     if (!S.row[k].ok) continue;
     const int64_t pi = int64_t(S.row[k].pbase) + int64_t(S.row[k].qh) * S.row[k].pstride;
     if constexpr (TR) {
@@ -779,7 +785,8 @@ __device__ __forceinline__ void lds_tile(MfmaState<D, NRTW>& S, const char* stag
   }
   bf16x8 pb[NACT], pl[NACT];
 #pragma unroll
-  for (int k = 0; k < NACT; ++k) mfma_softmax<D, NRTW, HILO>(S, k, s0[k], s1[k], a, it, base, j, pb[k], pl[k]);
+  for (int k = 0; k < NACT; ++k)
+    mfma_softmax<D, NRTW, HILO, NACT == 2>(S, k, s0[k], s1[k], a, it, base, j, pb[k], pl[k]);
   if constexpr (NACT == 2) {
     // V^T operands by LDS transpose reads: within each 16-lane group, lane L of
     // a ds_read_b64_tr_b16 receives element k = the (L % 4)-th 16-bit value at
@@ -803,6 +810,16 @@ __device__ __forceinline__ void lds_tile(MfmaState<D, NRTW>& S, const char* stag
       const bf16x8 vt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
       for (int k = 0; k < NACT; ++k) pv_update<D, NRTW, HILO>(S, k, db, vt, pb[k], pl[k]);
+    }
+    // l = ones x P^T: the row sums of the weights the P V product used, summed
+    // on the matrix cores in fp32 (the VALU sum they replace is 16 converts
+    // and adds per row tile)
+    const bf16x8 ones = {__bf16(1.0f), __bf16(1.0f), __bf16(1.0f), __bf16(1.0f),
+                         __bf16(1.0f), __bf16(1.0f), __bf16(1.0f), __bf16(1.0f)};
+#pragma unroll
+    for (int k = 0; k < NACT; ++k) {
+      S.L4[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[k], S.L4[k], 0, 0, 0);
+      if constexpr (HILO) S.L4[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pl[k], S.L4[k], 0, 0, 0);
     }
   } else {  // one row tile: v_perm from two 16-byte reads per token is the shorter chain
     VSlice<DPL> vs[8];
