@@ -30,11 +30,10 @@ constexpr int32_t kHiLoMinPath = 1024;
 // loop keeps kLdsStages - 1 tiles of 32 tokens in flight).
 constexpr int kLdsStages = 3;
 
-// The workgroup tile loop reads each wave's 16 page-table words of a tile
-// unconditionally, kLdsStages - 1 tiles ahead, so its reads reach at most
-// 63 + 32 * (kLdsStages - 2) words past a group's last token; the planner's
-// per-segment guard (kSegGuard words repeating the segment's last token)
-// covers them.
+// Page-table reads of the kernels are clamped to their chunk; the planner's
+// per-segment guard words (kSegGuard, repeating a written token of the
+// segment) are a margin for readers that run this many words past a
+// segment's end.
 constexpr int32_t kLookAheadWords = 63 + 32 * (kLdsStages - 2) + 1;
 
 struct PartialArgs {

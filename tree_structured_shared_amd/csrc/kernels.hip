@@ -27,9 +27,10 @@
 // Row arithmetic:
 //  * bf16: v_mfma_f32_16x16x32_bf16 on a transposed formulation, 16-row
 //    tiles (padded for fewer rows: the items are bound by their K/V stream).
-//    S^T = K Q^T: K rows are the A operand, loaded straight from the pool.
-//    O^T = V^T P^T: the score accumulators already sit in the B-operand
-//    layout of P^T, and V^T comes from a v_perm transpose of 16-byte V loads
+//    S^T = K Q^T: K rows are the A operand (straight from the pool, or from
+//    LDS). O^T = V^T P^T: the score accumulators already sit in the B-operand
+//    layout of P^T; V^T comes from a v_perm transpose of 16-byte V reads, or
+//    in workgroup waves with two row tiles from LDS transpose reads
 //    (stacking the queries that share KV turns the decode GEMV into a GEMM,
 //    FastTree review, kernel design).
 //  * fp32: wavefront dot products (GEMV), 8 lanes per token, DPP reductions,
@@ -57,6 +58,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBlock = 256;
@@ -692,22 +694,66 @@ __device__ __forceinline__ void mfma_wave(const PartialArgs& a, const WorkItem& 
 
 // ---------------------------------------------------------------------------
 // Workgroup items, bf16: one workgroup per item x kv-head, K/V tiles shared
-// through LDS. Each 32-token tile is loaded once by the whole workgroup (every
-// thread one token-row slice of 64 bytes) into one of two LDS stages; the next
-// tile is in flight in registers while the current one is computed, and one
-// barrier per tile hands the stage over. Token rows are stored with their
-// 16-byte chunks XOR-swizzled by the token index, so the stores and the MFMA
-// operand reads (16 lanes = 16 tokens or 16 chunks) hit distinct banks.
+// through LDS. Each 32-token tile is loaded once by the whole workgroup with
+// direct-to-LDS loads into one of kLdsStages stages (two tiles in flight while
+// one is computed), and one barrier per tile hands a stage over. Token rows
+// are stored with their 16-byte chunks XOR-swizzled by the token index, so the
+// MFMA operand reads (16 lanes = 16 tokens or 16 chunks) hit distinct banks.
+// A stage ends in each wave's page-table words for the tile two later.
 template <int D>
 struct LdsTile {
   static constexpr int CH = D / 8;         // 16-byte chunks per token row
   static constexpr int ROW = D * 2;        // bytes per token row
   static constexpr int PART = 32 * ROW;    // one K or V tile
-  static constexpr int STAGE = 2 * PART;   // K then V
+  static constexpr int WORDS = 256;        // per wave: the page-table words of a later tile
+  static constexpr int STAGE = 2 * PART + kWaves * WORDS;  // K, V, then the words
   static __device__ __forceinline__ int off(int part, int t, int c) {
     return part * PART + t * ROW + ((c ^ (t & (CH - 1))) << 4);
   }
 };
+
+// One direct-to-LDS load (global_load_lds_dwordx4): 16 bytes per lane from
+// base + off to the wave-uniform LDS address lds + 16 lane. Written as inline
+// asm so that the compiler does not track it: it would otherwise make every
+// LDS transpose read wait for all direct loads in flight (the tile loop's own
+// waits order the loads and the reads). M0 carries the LDS address and is
+// restored, as the compiler expects it unchanged.
+__device__ __forceinline__ void dma16(const char* base, uint32_t off, uint32_t lds) {
+  uint32_t m0_saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(m0_saved)
+      : "s"(lds), "v"(off), "s"(base)
+      : "memory");
+}
+__device__ __forceinline__ void dma16(const char* base, int64_t off, uint32_t lds) {
+  uint32_t m0_saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(m0_saved)
+      : "s"(lds), "v"(base + off)
+      : "memory");
+}
+
+// One direct-to-LDS load of 4 bytes per lane (global_load_lds_dword): from
+// base + off to lds + 4 lane; the same conventions as dma16.
+__device__ __forceinline__ void dma4(const int32_t* base, uint32_t off, uint32_t lds) {
+  uint32_t m0_saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dword %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(m0_saved)
+      : "s"(lds), "v"(off), "s"(base)
+      : "memory");
+}
 
 // Direct-to-LDS tile loads (global_load_lds_dwordx4): lane l of one
 // instruction writes 16 bytes at the wave-uniform LDS base + 16 l, so one
@@ -735,28 +781,22 @@ struct TileDma {
     wave = w;
   }
   // Wave w moves the K (w < 2) or V (w >= 2) rows of tokens 16 (w & 1) ..
-  // + 15 of the tile; e[] are their page-table words (wave-uniform, scalar
-  // loads: the wait for them never covers direct loads in flight). They go
-  // to lanes 0..15 of one register by v_writelane, and each lane takes its
-  // token's word by ds_bpermute (a per-lane select chain would be turned
-  // into a scratch lookup, a vector load).
-  __device__ __forceinline__ void issue(char* stage, const int32_t (&e)[16], const PartialArgs& a) const {
+  // + 15 of the tile; e[x] is the page-table word of the token the lane moves
+  // with its x-th instruction (token x * RPK + lane / CH of those 16).
+  __device__ __forceinline__ void issue(char* stage, const int32_t (&e)[NIW], const PartialArgs& a) const {
     typedef __attribute__((address_space(3))) char lds_char;
     const int lane = threadIdx.x & 63;
     const int r = lane / CH, p = lane % CH;
-    int32_t words = 0;
-#pragma unroll
-    for (int y = 0; y < 16; ++y) asm("v_writelane_b32 %0, %1, %2" : "+v"(words) : "s"(e[y]), "n"(y));
 #pragma unroll
     for (int x = 0; x < NIW; ++x) {
       const int m = wave * NIW + x;            // wave-uniform
       const int part = m / (NI / 2), blk = m % (NI / 2);
-      const int32_t sg = __builtin_amdgcn_ds_bpermute((x * RPK + r) << 2, words);
+      const int32_t sg = e[x];
       const int t = blk * RPK + r;
       const Off off = TokOff<FA>::of(sg, a) + Off(((p ^ (t & (CH - 1))) << 4));
-      const char* src = (part ? vb : kb) + off;
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
-                                       (lds_char*)(stage + part * L::PART + blk * 1024), 16, 0, 0);
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(
+          uint32_t(reinterpret_cast<uintptr_t>((lds_char*)(stage + part * L::PART + blk * 1024))));
+      dma16(part ? vb : kb, off, dst);
     }
   }
 };
@@ -853,13 +893,15 @@ __device__ __forceinline__ void lds_tile(MfmaState<D, NRTW>& S, const char* stag
 
 // The tile loop of a workgroup item: kLdsStages LDS stages filled by direct
 // loads kLdsStages - 1 tiles ahead. Per tile: wait for this wave's own
-// loads of the tile (explicit vmcnt: the compiler does not order LDS reads
-// after direct loads), one barrier (every wave's part of the tile has landed
-// and every wave is done with the stage the next loads overwrite), the next
-// loads, then the compute. Inside the loop no register depends on a vector
-// load (the compiler would wait for every direct load in flight before its
-// first use): page-table words come by scalar loads. NACT (row tiles this
-// wave computes) and HILO are fixed per loop.
+// loads of the tile (explicit vmcnt: the direct loads are invisible to the
+// compiler), one barrier (every wave's part of the tile has landed and every
+// wave is done with the stage the next loads overwrite), the next loads, then
+// the compute. The page-table words of tile t + 2 travel with tile t: each
+// wave's direct loads of a tile end with one 4-byte-per-lane load of the 16
+// words it needs two tiles later, into the stage's word area, so the words
+// are in LDS when the tile has landed and no load latency other than the
+// tiles' own is on the loop's path. NACT (row tiles this wave computes) and
+// HILO are fixed per loop.
 static_assert(kSegGuard >= kLookAheadWords, "the page-table guard covers the look-ahead reads");
 
 // s_waitcnt with vmcnt = n (< 16) and no wait on the other counters
@@ -884,41 +926,67 @@ template <int D, bool FA, int NACT, bool HILO>
 __device__ __forceinline__ void lds_stream(MfmaState<D, kBlockRowTiles>& S, char* lds, const PartialArgs& a,
                                            const WorkItem& it, int h, int i, int j) {
   typedef TileDma<D, FA> Dma;
-  constexpr int ST = LdsTile<D>::STAGE;
+  typedef LdsTile<D> L;
+  typedef __attribute__((address_space(3))) char lds_char;
+  constexpr int ST = L::STAGE, NIW = Dma::NIW;
   const int ntiles = (it.tok1 - it.tok0 + 31) >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // this wave's 16 tokens of each tile: page-table words by scalar loads.
-  // The page table is read-only for the kernel's lifetime: read it through
-  // the constant address space, so the uniform reads become scalar loads.
-  // Words past the chunk name other tokens of the segment, or (past the
-  // segment) its guard words, which repeat a written token: every load is of
-  // written K/V, and the softmax masks those tokens.
-  typedef const __attribute__((address_space(4))) int32_t cint32;
-  const cint32* st = (const cint32*)(a.seg_tok + __builtin_amdgcn_readfirstlane(it.seg_base));
-  const int first16 = __builtin_amdgcn_readfirstlane(it.tok0) + (wave & 1) * 16;
-  auto words = [&](int n, int32_t (&e)[16]) {
-    const cint32* p = st + first16 + n * 32;
-#pragma unroll
-    for (int y = 0; y < 16; ++y) e[y] = p[y];
+  const int lane = threadIdx.x & 63;
+  // Page-table words. Lane l of the words load fetches the word of token
+  // u = (l mod NIW) * RPK + (l mod 16) / NIW of this wave's 16, so the NIW
+  // words a lane needs for its direct loads (tokens x * RPK + lane / CH) are
+  // adjacent in LDS at 4 NIW (lane / CH). Indices are clamped to the chunk's
+  // last token: past it the loads fetch written K/V that the softmax masks.
+  static_assert(kLdsStages == 3, "the tile and word look-ahead here is written for three stages");
+  const int32_t* st = a.seg_tok;
+  const int seg0 = __builtin_amdgcn_readfirstlane(it.seg_base);
+  const int u = (lane % NIW) * Dma::RPK + (lane & 15) / NIW;
+  const int first = __builtin_amdgcn_readfirstlane(it.tok0) + (wave & 1) * 16 + u;
+  const int last = it.tok1 - 1;
+  auto word_off = [&](int n) -> uint32_t { return uint32_t(seg0 + min(first + n * 32, last)) * 4u; };
+  const int wpos = 2 * L::PART + wave * L::WORDS;           // this wave's word area in a stage
+  const int rpos = wpos + 4 * NIW * (lane / Dma::CH);        // this lane's NIW words there
+  auto lds_addr = [&](int stage_off) -> uint32_t {
+    return __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>((lds_char*)(lds + stage_off))));
   };
   Dma dma;
   dma.init(a, h, wave);
-  int32_t e[16];
-  // the unit's Q and row loads (and the previous unit's stores) retire
-  // here, so no register the loop reads waits on a vector load
-  wait_vmcnt<0>();
+  // tiles 0 and 1 take their words from plain loads; each later tile's come
+  // with the tile two before it
+  int32_t e[NIW], e1[NIW];
 #pragma unroll
-  for (int t = 0; t < kLdsStages - 1; ++t) {
-    words(t, e);
-    dma.issue(lds + t * ST, e, a);
+  for (int x = 0; x < NIW; ++x) {
+    const int tk = x * Dma::RPK + lane / Dma::CH;
+    const int b0 = __builtin_amdgcn_readfirstlane(it.tok0) + (wave & 1) * 16 + tk;
+    e[x] = st[seg0 + min(b0, last)];
+    e1[x] = st[seg0 + min(b0 + 32, last)];
   }
+  // the unit's Q and row loads, these words (and the previous unit's
+  // stores) retire here, so no register the loop reads waits on a vector load
+  wait_vmcnt<0>();
+  dma.issue(lds, e, a);
+  dma4(st, word_off(2), lds_addr(wpos));
+  dma.issue(lds + ST, e1, a);
+  dma4(st, word_off(3), lds_addr(ST + wpos));
   int stage = 0;
   for (int n = 0; n < ntiles; ++n) {
-    // this wave's loads of tile n landed (those of the kLdsStages - 2 tiles after it in flight)
-    lds_stage_barrier<(kLdsStages - 2) * Dma::NIW>();
-    words(n + kLdsStages - 1, e);
+    // this wave's loads of tile n (and the words of tile n + 2) landed; those
+    // of tile n + 1 in flight
+    lds_stage_barrier<NIW + 1>();
+    {
+      const char* wp = lds + stage * ST + rpos;
+      if constexpr (NIW == 4) {
+        const i32x4 w4 = *reinterpret_cast<const i32x4*>(wp);
+#pragma unroll
+        for (int x = 0; x < NIW; ++x) e[x] = w4[x];
+      } else {
+#pragma unroll
+        for (int x = 0; x < NIW; ++x) e[x] = reinterpret_cast<const int32_t*>(wp)[x];
+      }
+    }
     const int s2 = stage == 0 ? kLdsStages - 1 : stage - 1;  // the stage of tile n - 1, done by every wave
     dma.issue(lds + s2 * ST, e, a);
+    dma4(st, word_off(n + 4), lds_addr(s2 * ST + wpos));
     if constexpr (NACT > 0)
       lds_tile<D, kBlockRowTiles, NACT, HILO>(S, lds + stage * ST, a, it, it.tok0 + n * 32, i, j);
     stage = stage + 1 == kLdsStages ? 0 : stage + 1;
