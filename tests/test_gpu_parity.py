@@ -116,6 +116,36 @@ def test_row_paths(dtype, d, rows_case):
     _check(_run(inst, rb=256, split=False), ref, f"rows {rows_case} {dtype} d{d} rb256 nosplit")
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_reduction_pairs_per_wave(dtype):
+    """The reduction packs 4, 2 or 1 (query, q-head) pairs per wave by the
+    plan's largest slot count per query (at most 4, 8, or more). Cover all
+    three, each with a pair count that is not a multiple of the packing (the
+    wave's last groups have no pair)."""
+    cases = [
+        # (parent, lens, qpl, n_qheads, n_kvheads, plan options)
+        ([-1, 0, 0], [40, 20, 30], 1, 1, 1, {}),                                  # 2 pairs, <= 4 slots
+        ([-1, 0, 0, 1, 1, 2], [70, 20, 30, 9, 17, 25], 2, 3, 1, {}),              # 18 pairs
+        ([-1, 0, 0, 0], [900, 40, 70, 33], 1, 3, 3,
+         dict(waves=2, ncu=8, floor_f=0, split_align=16)),                        # 9 pairs, 6 slots
+        ([-1, 0, 1, 1], [2000, 300, 40, 70], 1, 5, 5,
+         dict(waves=64, floor_f=0, split_align=16)),                              # 10 pairs, long paths
+    ]
+    seen = set()
+    for x, (parent, lens, qpl, hq, hk, kw) in enumerate(cases):
+        inst = synth.make_tree(parent, lens, page_size=16, qpl=qpl, n_qheads=hq, n_kvheads=hk,
+                               head_dim=128 if dtype == torch.bfloat16 else 64, dtype=dtype, seed=40 + x)
+        synth.fill_tensors(inst, seed=50 + x)
+        plan = Plan.for_instance(inst, host_only=True, **kw)
+        ms = int(np.diff(plan.export("q_slot_ptr")).max())
+        plan.close()
+        packing = 4 if ms <= 4 else (2 if ms <= 8 else 1)
+        seen.add(packing)
+        _log(f"case {x}: {inst.n_queries} queries x {hq} q-heads, max {ms} slots per query, {packing} pairs per wave")
+        _check(_run(inst, **kw), ta.decode_instance(inst), f"pairs-per-wave case {x}")
+    assert seen == {1, 2, 4}, seen
+
+
 def test_edge_cases():
     cases = [
         ([-1], [1], 1),                 # one node, one token

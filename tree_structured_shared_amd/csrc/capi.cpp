@@ -28,6 +28,12 @@ ta_status hip_err(hipError_t e, const char* where) {
   return set_err(TA_EHIP, std::string(where) + ": " + hipGetErrorString(e));
 }
 
+int32_t max_slot_count(const std::vector<int32_t>& ptr) {
+  int32_t m = 0;
+  for (size_t x = 0; x + 1 < ptr.size(); ++x) m = std::max(m, ptr[x + 1] - ptr[x]);
+  return m;
+}
+
 }  // namespace
 
 struct ta_plan {
@@ -48,6 +54,7 @@ struct ta_plan {
   // host copies of what the device holds in the item and slot-position regions
   std::vector<ta::WorkItem> h_items;
   std::vector<int32_t> h_slot_pos, h_vis, h_q_slot_ptr;
+  int32_t max_slots = 0;  // largest slot count of one query in h_q_slot_ptr
   void* d_ws = nullptr;  // workspace: o_part | m_part | l_part
   float *d_o_part = nullptr, *d_m_part = nullptr, *d_l_part = nullptr;
   int64_t ws_bytes = 0, ws_cap = 0;
@@ -217,6 +224,7 @@ ta_status upload_full(ta_plan* p, bool headroom, bool* moved) {
   device_forms(p);
   p->h_vis = T.group_vis;
   p->h_q_slot_ptr = T.q_slot_ptr;
+  p->max_slots = max_slot_count(T.q_slot_ptr);
   size_t need[6];
   region_sizes(p, need);
   bool fits = p->d_tables != nullptr && !headroom;  // growth always re-sizes
@@ -296,6 +304,7 @@ ta_status upload_incremental(ta_plan* p, hipStream_t s) {
           size_t(T.seg_dirty[x + 1] - T.seg_dirty[x]));
   p->h_vis = T.group_vis;
   p->h_q_slot_ptr = T.q_slot_ptr;
+  p->max_slots = max_slot_count(T.q_slot_ptr);
   if (desc.empty()) return TA_OK;
   const int32_t n_desc = int32_t(desc.size() / 3);
   for (int32_t d = 0; d < n_desc; ++d) desc[3 * d + 2] += int32_t(desc.size());  // data after descriptors
@@ -563,6 +572,7 @@ ta_status tree_attn_decode(const void* q, ta_dtype q_dtype, const ta_paged_kv* k
   r.out = out;
   r.n_queries = plan->T.n_queries;
   r.n_qheads = plan->n_qheads;
+  r.max_slots = plan->max_slots;
   e = ta::launch_reduce(r, plan->head_dim, s, t_red);
   if (e != hipSuccess) return hip_err(e, "tree_attn_decode: reduction launch");
   if (timed) ++mp->timing_n;

@@ -26,15 +26,12 @@ struct WorkItem {
 // away, so such queries get the exact two-term (hi + lo) product.
 constexpr int32_t kHiLoMinPath = 1024;
 
-// LDS stages of the workgroup tile loop (16 KiB each at head_dim 128; the
-// loop keeps kLdsStages - 1 tiles of 32 tokens in flight).
+// LDS stages of the workgroup tile loop (17 KiB each at head_dim 128: K, V
+// and page-table words of 32 tokens; the loop keeps kLdsStages - 1 tiles in
+// flight while one is computed). Every page-table read of the kernels is
+// clamped to its chunk's last token; the planner's per-segment guard words
+// (kSegGuard, repeating a written token of the segment) are a margin beyond.
 constexpr int kLdsStages = 3;
-
-// Page-table reads of the kernels are clamped to their chunk; the planner's
-// per-segment guard words (kSegGuard, repeating a written token of the
-// segment) are a margin for readers that run this many words past a
-// segment's end.
-constexpr int32_t kLookAheadWords = 63 + 32 * (kLdsStages - 2) + 1;
 
 struct PartialArgs {
   const WorkItem* items;
@@ -66,6 +63,7 @@ struct ReduceArgs {
   const float* l_part;
   float* out;  // [n_q, n_qheads, D]
   int32_t n_queries, n_qheads;
+  int32_t max_slots;  // largest slot count of one query (sets the pairs per wave)
 };
 
 // Each launcher takes an optional pair of timing events (both null or both

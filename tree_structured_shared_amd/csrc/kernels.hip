@@ -896,13 +896,14 @@ __device__ __forceinline__ void lds_tile(MfmaState<D, NRTW>& S, const char* stag
 // loads of the tile (explicit vmcnt: the direct loads are invisible to the
 // compiler), one barrier (every wave's part of the tile has landed and every
 // wave is done with the stage the next loads overwrite), the next loads, then
-// the compute. The page-table words of tile t + 2 travel with tile t: each
-// wave's direct loads of a tile end with one 4-byte-per-lane load of the 16
-// words it needs two tiles later, into the stage's word area, so the words
-// are in LDS when the tile has landed and no load latency other than the
-// tiles' own is on the loop's path. NACT (row tiles this wave computes) and
-// HILO are fixed per loop.
-static_assert(kSegGuard >= kLookAheadWords, "the page-table guard covers the look-ahead reads");
+// the compute. The page-table words of tile t + AHEAD (AHEAD = kLdsStages -
+// 1) travel with tile t: each wave's direct loads of a tile end with one
+// 4-byte-per-lane load of the 16 words it needs AHEAD tiles later, into the
+// stage's word area, so the words are in LDS when the tile has landed and no
+// load latency other than the tiles' own is on the loop's path. Every
+// page-table read is clamped to the chunk's last token (loads past the last
+// tile fetch written K/V that the softmax never uses). NACT (row tiles this
+// wave computes) and HILO are fixed per loop.
 
 // s_waitcnt with vmcnt = n (< 16) and no wait on the other counters
 template <int N>
@@ -937,7 +938,8 @@ __device__ __forceinline__ void lds_stream(MfmaState<D, kBlockRowTiles>& S, char
   // words a lane needs for its direct loads (tokens x * RPK + lane / CH) are
   // adjacent in LDS at 4 NIW (lane / CH). Indices are clamped to the chunk's
   // last token: past it the loads fetch written K/V that the softmax masks.
-  static_assert(kLdsStages == 3, "the tile and word look-ahead here is written for three stages");
+  constexpr int NS = kLdsStages, AHEAD = NS - 1;  // loads (and the words they carry) run AHEAD tiles ahead
+  static_assert(NS >= 3 && (AHEAD - 1) * (NIW + 1) < 16, "the loop's wait fits the vmcnt field");
   const int32_t* st = a.seg_tok;
   const int seg0 = __builtin_amdgcn_readfirstlane(it.seg_base);
   const int u = (lane % NIW) * Dma::RPK + (lane & 15) / NIW;
@@ -951,45 +953,47 @@ __device__ __forceinline__ void lds_stream(MfmaState<D, kBlockRowTiles>& S, char
   };
   Dma dma;
   dma.init(a, h, wave);
-  // tiles 0 and 1 take their words from plain loads; each later tile's come
-  // with the tile two before it
-  int32_t e[NIW], e1[NIW];
+  // tiles 0 .. AHEAD - 1 take their words from plain loads; each later
+  // tile's come with the tile AHEAD before it
+  int32_t e[AHEAD][NIW];
 #pragma unroll
   for (int x = 0; x < NIW; ++x) {
     const int tk = x * Dma::RPK + lane / Dma::CH;
     const int b0 = __builtin_amdgcn_readfirstlane(it.tok0) + (wave & 1) * 16 + tk;
-    e[x] = st[seg0 + min(b0, last)];
-    e1[x] = st[seg0 + min(b0 + 32, last)];
+#pragma unroll
+    for (int t = 0; t < AHEAD; ++t) e[t][x] = st[seg0 + min(b0 + 32 * t, last)];
   }
   // the unit's Q and row loads, these words (and the previous unit's
   // stores) retire here, so no register the loop reads waits on a vector load
   wait_vmcnt<0>();
-  dma.issue(lds, e, a);
-  dma4(st, word_off(2), lds_addr(wpos));
-  dma.issue(lds + ST, e1, a);
-  dma4(st, word_off(3), lds_addr(ST + wpos));
+#pragma unroll
+  for (int t = 0; t < AHEAD; ++t) {
+    dma.issue(lds + t * ST, e[t], a);
+    dma4(st, word_off(t + AHEAD), lds_addr(t * ST + wpos));
+  }
   int stage = 0;
   for (int n = 0; n < ntiles; ++n) {
-    // this wave's loads of tile n (and the words of tile n + 2) landed; those
-    // of tile n + 1 in flight
-    lds_stage_barrier<NIW + 1>();
+    // this wave's loads of tile n (and the words of tile n + AHEAD) landed;
+    // those of the next AHEAD - 1 tiles in flight
+    lds_stage_barrier<(AHEAD - 1) * (NIW + 1)>();
+    int32_t w[NIW];
     {
       const char* wp = lds + stage * ST + rpos;
       if constexpr (NIW == 4) {
         const i32x4 w4 = *reinterpret_cast<const i32x4*>(wp);
 #pragma unroll
-        for (int x = 0; x < NIW; ++x) e[x] = w4[x];
+        for (int x = 0; x < NIW; ++x) w[x] = w4[x];
       } else {
 #pragma unroll
-        for (int x = 0; x < NIW; ++x) e[x] = reinterpret_cast<const int32_t*>(wp)[x];
+        for (int x = 0; x < NIW; ++x) w[x] = reinterpret_cast<const int32_t*>(wp)[x];
       }
     }
-    const int s2 = stage == 0 ? kLdsStages - 1 : stage - 1;  // the stage of tile n - 1, done by every wave
-    dma.issue(lds + s2 * ST, e, a);
-    dma4(st, word_off(n + 4), lds_addr(s2 * ST + wpos));
+    const int sf = stage == 0 ? NS - 1 : stage - 1;  // the stage of tile n - 1, done by every wave
+    dma.issue(lds + sf * ST, w, a);
+    dma4(st, word_off(n + 2 * AHEAD), lds_addr(sf * ST + wpos));
     if constexpr (NACT > 0)
       lds_tile<D, kBlockRowTiles, NACT, HILO>(S, lds + stage * ST, a, it, it.tok0 + n * 32, i, j);
-    stage = stage + 1 == kLdsStages ? 0 : stage + 1;
+    stage = stage + 1 == NS ? 0 : stage + 1;
   }
   // every wave's direct loads (the clamped ones past the end included) land
   // before the stages are reused
@@ -1091,39 +1095,52 @@ __global__ __launch_bounds__(kBlock, 2) void partial_kernel(PartialArgs a, int n
 }
 
 // ---------------------------------------------------------------------------
-// One wave per (query, q-head). The wave's four 16-lane groups take every
-// fourth of the query's slots (each lane D/16 consecutive output elements),
-// loading them in batches of 4 so the loads are in flight together; the
-// groups' (M, L, acc) are then merged with two permlane swaps and group 0
-// writes the normalised output.
+// P (query, q-head) pairs per wave (P = 1, 2, 4): each pair gets 4 / P of the
+// wave's 16-lane groups, which take every (4 / P)-th of the query's slots
+// (each lane D/16 consecutive output elements), loading them in batches of 4
+// so the loads are in flight together; a pair's groups are then merged with
+// permlane swaps and its first group writes the normalised output. The host
+// picks P from the plan's largest slot count per query, so that one batch
+// covers every pair where it can: short paths then take a quarter of the
+// waves, and long ones keep all four groups on one pair.
 constexpr int kReduceBatch = 4;
 constexpr int kReduceGroups = 4;
 
-template <int D>
+template <int D, int P>
 __global__ __launch_bounds__(kBlock) void lse_reduce_kernel(ReduceArgs a) {
-  constexpr int EPL = D / 16;      // output elements per lane
-  const int pair = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (pair >= a.n_queries * a.n_qheads) return;
+  static_assert(P == 1 || P == 2 || P == 4, "pairs per wave");
+  constexpr int EPL = D / 16;         // output elements per lane
+  constexpr int GP = kReduceGroups / P;  // lane groups per pair
+  const int64_t n_pairs = int64_t(a.n_queries) * a.n_qheads;
+  const int64_t wave_id = int64_t(blockIdx.x) * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wave_id * P >= n_pairs) return;
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, sub = lane & 15;
-  const int q = pair / a.n_qheads;
-  const int hq = pair - q * a.n_qheads;
+  const int sg = g % GP;              // this group's place among its pair's groups
+  const int64_t pair = wave_id * P + g / GP;
+  const bool live = pair < n_pairs;   // the wave's last pairs may lie past the end
+  const int q = live ? int(pair / a.n_qheads) : 0;
+  const int hq = live ? int(pair - int64_t(q) * a.n_qheads) : 0;
+  int s0 = a.q_slot_ptr[q];
+  int s1 = live ? a.q_slot_ptr[q + 1] : s0;
+  if constexpr (P == 1) {
+    s0 = __builtin_amdgcn_readfirstlane(s0);
+    s1 = __builtin_amdgcn_readfirstlane(s1);
+  }
   float M = TA_NEG_INF, L = 0.0f;
   float acc[EPL];
 #pragma unroll
   for (int x = 0; x < EPL; ++x) acc[x] = 0.0f;
-  const int s0 = __builtin_amdgcn_readfirstlane(a.q_slot_ptr[q]);
-  const int s1 = __builtin_amdgcn_readfirstlane(a.q_slot_ptr[q + 1]);
-  for (int b = s0 + g; b < s1; b += kReduceGroups * kReduceBatch) {
+  for (int b = s0 + sg; b < s1; b += GP * kReduceBatch) {
     int64_t pi[kReduceBatch];
 #pragma unroll
     for (int u = 0; u < kReduceBatch; ++u)
-      pi[u] = int64_t(s0) * a.n_qheads + int64_t(hq) * (s1 - s0) + (min(b + kReduceGroups * u, s1 - 1) - s0);
+      pi[u] = int64_t(s0) * a.n_qheads + int64_t(hq) * (s1 - s0) + (min(b + GP * u, s1 - 1) - s0);
     float mv[kReduceBatch], lv[kReduceBatch];
     f32x4 ov[kReduceBatch][EPL / 4];
 #pragma unroll
     for (int u = 0; u < kReduceBatch; ++u) {
-      mv[u] = (b + kReduceGroups * u < s1) ? a.m_part[pi[u]] : TA_NEG_INF;
+      mv[u] = (b + GP * u < s1) ? a.m_part[pi[u]] : TA_NEG_INF;
       lv[u] = a.l_part[pi[u]];
 #pragma unroll
       for (int c = 0; c < EPL / 4; ++c)
@@ -1147,9 +1164,10 @@ __global__ __launch_bounds__(kBlock) void lse_reduce_kernel(ReduceArgs a) {
     }
     M = Mn;
   }
-  // merge the four slot groups (lanes sub, sub+16, sub+32, sub+48)
+  // merge a pair's groups: lanes sub + 16 g over its GP groups (GP = 4: two
+  // swaps; GP = 2: groups 2k and 2k + 1 by one swap)
 #pragma unroll
-  for (int step = 0; step < 2; ++step) {
+  for (int step = 0; (1 << step) < GP; ++step) {
     const float Mo = step == 0 ? xor16(M) : xor32(M);
     const float Lo = step == 0 ? xor16(L) : xor32(L);
     const float Mn = fmaxf(M, Mo);
@@ -1162,7 +1180,7 @@ __global__ __launch_bounds__(kBlock) void lse_reduce_kernel(ReduceArgs a) {
     }
     M = Mn;
   }
-  if (g == 0) {
+  if (sg == 0 && live) {
     const float inv = 1.0f / L;
     float* op = a.out + (int64_t(q) * a.n_qheads + hq) * D + sub * EPL;
 #pragma unroll
@@ -1227,6 +1245,20 @@ void launch_partial_t(const PartialArgs& a, int32_t n_block_items, int32_t n_wav
                           n_units);
 }
 
+template <int D, int P>
+void launch_reduce_t(const ReduceArgs& a, int64_t pairs, hipStream_t s, KernelTimer t) {
+  const int64_t waves = (pairs + P - 1) / P;
+  const dim3 grid(unsigned((waves + kWaves - 1) / kWaves)), block(kBlock);
+  hipExtLaunchKernelGGL((lse_reduce_kernel<D, P>), grid, block, 0, s, t.start, t.stop, 0, a);
+}
+
+template <int D>
+void launch_reduce_d(const ReduceArgs& a, int64_t pairs, hipStream_t s, KernelTimer t) {
+  if (a.max_slots <= kReduceBatch) launch_reduce_t<D, 4>(a, pairs, s, t);
+  else if (a.max_slots <= 2 * kReduceBatch) launch_reduce_t<D, 2>(a, pairs, s, t);
+  else launch_reduce_t<D, 1>(a, pairs, s, t);
+}
+
 }  // namespace
 
 hipError_t launch_partial(const PartialArgs& a, int32_t n_block_items, int32_t n_wave_items, int dtype,
@@ -1245,9 +1277,8 @@ hipError_t launch_partial(const PartialArgs& a, int32_t n_block_items, int32_t n
 hipError_t launch_reduce(const ReduceArgs& a, int head_dim, hipStream_t s, KernelTimer t) {
   const int64_t pairs = int64_t(a.n_queries) * a.n_qheads;
   if (pairs <= 0) return hipSuccess;
-  const dim3 grid(unsigned((pairs + kWaves - 1) / kWaves)), block(kBlock);
-  if (head_dim == 128) hipExtLaunchKernelGGL(lse_reduce_kernel<128>, grid, block, 0, s, t.start, t.stop, 0, a);
-  else hipExtLaunchKernelGGL(lse_reduce_kernel<64>, grid, block, 0, s, t.start, t.stop, 0, a);
+  if (head_dim == 128) launch_reduce_d<128>(a, pairs, s, t);
+  else launch_reduce_d<64>(a, pairs, s, t);
   return hipGetLastError();
 }
 
