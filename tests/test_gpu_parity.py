@@ -119,15 +119,20 @@ def test_row_paths(dtype, d, rows_case):
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_reduction_pairs_per_wave(dtype):
     """The reduction packs 4, 2 or 1 (query, q-head) pairs per wave by the
-    plan's largest slot count per query (at most 4, 8, or more). Cover all
-    three, each with a pair count that is not a multiple of the packing (the
-    wave's last groups have no pair)."""
+    plan's largest slot count per query (at most 4, 8, or more), and loads
+    batches of 4, 8 or 16 slots per lane group (one pair per wave with up to
+    16, 32 or more slots). Cover every kernel variant, with pair counts that
+    are not a multiple of the packing (the wave's last groups have no pair)."""
     cases = [
         # (parent, lens, qpl, n_qheads, n_kvheads, plan options)
         ([-1, 0, 0], [40, 20, 30], 1, 1, 1, {}),                                  # 2 pairs, <= 4 slots
         ([-1, 0, 0, 1, 1, 2], [70, 20, 30, 9, 17, 25], 2, 3, 1, {}),              # 18 pairs
         ([-1, 0, 0, 0], [900, 40, 70, 33], 1, 3, 3,
          dict(waves=2, ncu=8, floor_f=0, split_align=16)),                        # 9 pairs, 6 slots
+        ([-1, 0, 1, 1], [300, 300, 40, 70], 1, 5, 5,
+         dict(waves=2, ncu=32, floor_f=0, split_align=16)),                       # 10 pairs, 12 slots
+        ([-1, 0, 1, 1], [300, 300, 40, 70], 1, 5, 5,
+         dict(waves=4, ncu=32, floor_f=0, split_align=16)),                       # 22 slots
         ([-1, 0, 1, 1], [2000, 300, 40, 70], 1, 5, 5,
          dict(waves=64, floor_f=0, split_align=16)),                              # 10 pairs, long paths
     ]
@@ -139,11 +144,12 @@ def test_reduction_pairs_per_wave(dtype):
         plan = Plan.for_instance(inst, host_only=True, **kw)
         ms = int(np.diff(plan.export("q_slot_ptr")).max())
         plan.close()
-        packing = 4 if ms <= 4 else (2 if ms <= 8 else 1)
-        seen.add(packing)
-        _log(f"case {x}: {inst.n_queries} queries x {hq} q-heads, max {ms} slots per query, {packing} pairs per wave")
+        variant = (4, 4) if ms <= 4 else (2, 4) if ms <= 8 else (1, 4) if ms <= 16 else (1, 8) if ms <= 32 else (1, 16)
+        seen.add(variant)
+        _log(f"case {x}: {inst.n_queries} queries x {hq} q-heads, max {ms} slots per query, "
+             f"(pairs per wave, batch) {variant}")
         _check(_run(inst, **kw), ta.decode_instance(inst), f"pairs-per-wave case {x}")
-    assert seen == {1, 2, 4}, seen
+    assert seen == {(4, 4), (2, 4), (1, 4), (1, 8), (1, 16)}, seen
 
 
 def test_edge_cases():

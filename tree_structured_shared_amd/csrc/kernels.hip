@@ -610,7 +610,7 @@ __device__ __forceinline__ void mfma_tile(MfmaState<D, NRTW>& S, const TileKV<D>
 // for younger K/V data, and two tiles stay in flight while one is computed.
 template <int D, int NRTW, bool FA, bool HILO>
 __device__ __forceinline__ void mfma_stream(MfmaState<D, NRTW>& S, const PartialArgs& a, const WorkItem& it,
-                                            int h) {
+                                            int h, TileSeg sgA, TileSeg sgB) {
   const int lane = threadIdx.x & 63;
   const int i = lane & 15, j = lane >> 4;
   const int ntiles = (it.tok1 - it.tok0 + 31) >> 5;
@@ -619,13 +619,10 @@ __device__ __forceinline__ void mfma_stream(MfmaState<D, NRTW>& S, const Partial
   const int32_t* st = a.seg_tok + it.seg_base;
   const int last = it.tok1 - 1;
 
-  // issue order: seg 0, seg 1, kv 0, seg 2, kv 1, seg 3, then per tile n:
-  // compute n, kv n + 2, seg n + 4
-  TileSeg sgA, sgB;
+  // issue order: seg 0, seg 1 (by the caller, beside the row and Q loads),
+  // kv 0, seg 2, kv 1, seg 3, then per tile n: compute n, kv n + 2, seg n + 4
   TileKV<D> bA, bB;
   int base = it.tok0;
-  load_tile_seg(sgA, st, base, last, i, j);
-  load_tile_seg(sgB, st, base + 32, last, i, j);
   load_tile_kv<D, FA>(bA, sgA, kb, vb, j, i, a);
   load_tile_seg(sgA, st, base + 64, last, i, j);
   load_tile_kv<D, FA>(bB, sgB, kb, vb, j, i, a);
@@ -685,10 +682,17 @@ __device__ __forceinline__ void mfma_write(MfmaState<D, NRTW>& S, const PartialA
 template <int D, int NRTW, bool FA>
 __device__ __forceinline__ void mfma_wave(const PartialArgs& a, const WorkItem& it, int h, const int (&rt)[NRTW],
                                           const bool (&on)[NRTW]) {
+  // the first two tiles' page-table entries depend only on the item: they
+  // are requested together with the row references, so the first K/V loads
+  // can follow the Q loads instead of waiting one more round trip
+  const int lane = threadIdx.x & 63;
+  TileSeg sgA, sgB;
+  load_tile_seg(sgA, a.seg_tok + it.seg_base, it.tok0, it.tok1 - 1, lane & 15, lane >> 4);
+  load_tile_seg(sgB, a.seg_tok + it.seg_base, it.tok0 + 32, it.tok1 - 1, lane & 15, lane >> 4);
   MfmaState<D, NRTW> S;
   mfma_init(S, a, it, h, rt, on);
-  if (it.flags & 1) mfma_stream<D, NRTW, FA, true>(S, a, it, h);
-  else mfma_stream<D, NRTW, FA, false>(S, a, it, h);
+  if (it.flags & 1) mfma_stream<D, NRTW, FA, true>(S, a, it, h, sgA, sgB);
+  else mfma_stream<D, NRTW, FA, false>(S, a, it, h, sgA, sgB);
   mfma_write(S, a);
 }
 
@@ -1097,18 +1101,18 @@ __global__ __launch_bounds__(kBlock, 2) void partial_kernel(PartialArgs a, int n
 // ---------------------------------------------------------------------------
 // P (query, q-head) pairs per wave (P = 1, 2, 4): each pair gets 4 / P of the
 // wave's 16-lane groups, which take every (4 / P)-th of the query's slots
-// (each lane D/16 consecutive output elements), loading them in batches of 4
+// (each lane D/16 consecutive output elements), loading them in batches of B
 // so the loads are in flight together; a pair's groups are then merged with
 // permlane swaps and its first group writes the normalised output. The host
-// picks P from the plan's largest slot count per query, so that one batch
-// covers every pair where it can: short paths then take a quarter of the
-// waves, and long ones keep all four groups on one pair.
-constexpr int kReduceBatch = 4;
+// picks P and B from the plan's largest slot count per query, so that one
+// batch covers every pair where it can: short paths take a quarter of the
+// waves, long ones keep all four groups on one pair with deeper batches.
 constexpr int kReduceGroups = 4;
 
-template <int D, int P>
+template <int D, int P, int B>
 __global__ __launch_bounds__(kBlock) void lse_reduce_kernel(ReduceArgs a) {
   static_assert(P == 1 || P == 2 || P == 4, "pairs per wave");
+  constexpr int kReduceBatch = B;
   constexpr int EPL = D / 16;         // output elements per lane
   constexpr int GP = kReduceGroups / P;  // lane groups per pair
   const int64_t n_pairs = int64_t(a.n_queries) * a.n_qheads;
@@ -1245,18 +1249,23 @@ void launch_partial_t(const PartialArgs& a, int32_t n_block_items, int32_t n_wav
                           n_units);
 }
 
-template <int D, int P>
+template <int D, int P, int B>
 void launch_reduce_t(const ReduceArgs& a, int64_t pairs, hipStream_t s, KernelTimer t) {
   const int64_t waves = (pairs + P - 1) / P;
   const dim3 grid(unsigned((waves + kWaves - 1) / kWaves)), block(kBlock);
-  hipExtLaunchKernelGGL((lse_reduce_kernel<D, P>), grid, block, 0, s, t.start, t.stop, 0, a);
+  hipExtLaunchKernelGGL((lse_reduce_kernel<D, P, B>), grid, block, 0, s, t.start, t.stop, 0, a);
 }
 
+// one batch per group where the slots allow: up to 4 slots 4 pairs per
+// wave, up to 8 two, then one pair with batches of 4, 8 or 16 slots per group
 template <int D>
 void launch_reduce_d(const ReduceArgs& a, int64_t pairs, hipStream_t s, KernelTimer t) {
-  if (a.max_slots <= kReduceBatch) launch_reduce_t<D, 4>(a, pairs, s, t);
-  else if (a.max_slots <= 2 * kReduceBatch) launch_reduce_t<D, 2>(a, pairs, s, t);
-  else launch_reduce_t<D, 1>(a, pairs, s, t);
+  const int32_t m = a.max_slots;
+  if (m <= 4) launch_reduce_t<D, 4, 4>(a, pairs, s, t);
+  else if (m <= 8) launch_reduce_t<D, 2, 4>(a, pairs, s, t);
+  else if (m <= 16) launch_reduce_t<D, 1, 4>(a, pairs, s, t);
+  else if (m <= 32) launch_reduce_t<D, 1, 8>(a, pairs, s, t);
+  else launch_reduce_t<D, 1, 16>(a, pairs, s, t);
 }
 
 }  // namespace
