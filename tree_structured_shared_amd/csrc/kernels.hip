@@ -641,18 +641,19 @@ __device__ __forceinline__ void mfma_stream(MfmaState<D, NRTW>& S, const Partial
 }
 
 // lane (i, j) holds O[k][db][c] = O[row i][d], with d = DPL * (4j + c) + db
-// when V^T came from v_perm (single-wave items), d = 16 db + 4j + c when it
-// came from LDS transpose reads (workgroup items, TR). Without TR l is
-// lane-partial (its 8 tokens per tile) and is summed over the row's 4 lanes;
-// with TR it comes whole from the ones x P^T accumulator.
-template <int D, int NRTW, bool TR = false>
+// when V^T came from v_perm, d = 16 db + 4j + c when it came from LDS
+// transpose reads (workgroup waves with two row tiles, TR). With LM (every
+// workgroup wave) l comes whole from the ones x P^T accumulator; without it
+// (single-wave items) l is lane-partial (its 8 tokens per tile) and is summed
+// over the row's 4 lanes.
+template <int D, int NRTW, bool TR = false, bool LM = TR>
 __device__ __forceinline__ void mfma_write(MfmaState<D, NRTW>& S, const PartialArgs& a) {
   constexpr int DPL = D / 16;
   const int j = (threadIdx.x & 63) >> 4;
 #pragma unroll
   for (int k = 0; k < NRTW; ++k) {
     if (!S.on[k]) continue;
-    const float l = TR ? S.L4[k][0] : sum4rows(S.l[k]);
+    const float l = LM ? S.L4[k][0] : sum4rows(S.l[k]);
     if (!S.row[k].ok) continue;
     const int64_t pi = int64_t(S.row[k].pbase) + int64_t(S.row[k].qh) * S.row[k].pstride;
     if constexpr (TR) {
@@ -830,7 +831,7 @@ __device__ __forceinline__ void lds_tile(MfmaState<D, NRTW>& S, const char* stag
   bf16x8 pb[NACT], pl[NACT];
 #pragma unroll
   for (int k = 0; k < NACT; ++k)
-    mfma_softmax<D, NRTW, HILO, NACT == 2>(S, k, s0[k], s1[k], a, it, base, j, pb[k], pl[k]);
+    mfma_softmax<D, NRTW, HILO, true>(S, k, s0[k], s1[k], a, it, base, j, pb[k], pl[k]);
   if constexpr (NACT == 2) {
     // V^T operands by LDS transpose reads: within each 16-lane group, lane L of
     // a ds_read_b64_tr_b16 receives element k = the (L % 4)-th 16-bit value at
@@ -854,16 +855,6 @@ __device__ __forceinline__ void lds_tile(MfmaState<D, NRTW>& S, const char* stag
       const bf16x8 vt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
       for (int k = 0; k < NACT; ++k) pv_update<D, NRTW, HILO>(S, k, db, vt, pb[k], pl[k]);
-    }
-    // l = ones x P^T: the row sums of the weights the P V product used, summed
-    // on the matrix cores in fp32 (the VALU sum they replace is 16 converts
-    // and adds per row tile)
-    const bf16x8 ones = {__bf16(1.0f), __bf16(1.0f), __bf16(1.0f), __bf16(1.0f),
-                         __bf16(1.0f), __bf16(1.0f), __bf16(1.0f), __bf16(1.0f)};
-#pragma unroll
-    for (int k = 0; k < NACT; ++k) {
-      S.L4[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[k], S.L4[k], 0, 0, 0);
-      if constexpr (HILO) S.L4[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pl[k], S.L4[k], 0, 0, 0);
     }
   } else {  // one row tile: v_perm from two 16-byte reads per token is the shorter chain
     VSlice<DPL> vs[8];
@@ -892,6 +883,16 @@ __device__ __forceinline__ void lds_tile(MfmaState<D, NRTW>& S, const char* stag
         pv_update<D, NRTW, HILO>(S, k, 2 * w + 1, vhi, pb[k], pl[k]);
       }
     }
+  }
+  // l = ones x P^T: the row sums of the weights the P V product used, summed
+  // on the matrix cores in fp32 (the VALU sum they replace is 16 converts
+  // and adds per row tile)
+  const bf16x8 ones = {__bf16(1.0f), __bf16(1.0f), __bf16(1.0f), __bf16(1.0f),
+                       __bf16(1.0f), __bf16(1.0f), __bf16(1.0f), __bf16(1.0f)};
+#pragma unroll
+  for (int k = 0; k < NACT; ++k) {
+    S.L4[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[k], S.L4[k], 0, 0, 0);
+    if constexpr (HILO) S.L4[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pl[k], S.L4[k], 0, 0, 0);
   }
 }
 
@@ -1036,9 +1037,10 @@ __device__ __forceinline__ void block_lds_item(const PartialArgs& a, char* lds, 
     } else {
       lds_stream<D, FA, 0, false>(S, lds, a, it, h, i, j);
     }
-    // waves with two row tiles built V^T by transpose reads (d = 16 db + 4j + c)
+    // waves with two row tiles built V^T by transpose reads (d = 16 db + 4j + c);
+    // every workgroup wave summed l on the matrix cores
     if (S.on[1]) mfma_write<D, kBlockRowTiles, true>(S, a);
-    else mfma_write<D, kBlockRowTiles, false>(S, a);
+    else mfma_write<D, kBlockRowTiles, false, true>(S, a);
   }
 }
 
