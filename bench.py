@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of the MI355X
 METRIC = "tree-decode attn: µs/step + effective HBM GB/s (unique KV bytes) vs peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "partial_kernel_traffic.json")
 
@@ -116,6 +117,31 @@ def head_major_pool(pool, dev):
     returned as a [n_pages, page_size, H, d] view: the layout the library is
     timed on (the C ABI takes any pool strides with head_dim contiguous)."""
     return pool.permute(0, 2, 1, 3).contiguous().to(dev).permute(0, 2, 1, 3)
+
+
+def algorithmic_flops(inst):
+    """Flops one decode step must do: every query's q-heads against every
+    token it sees, QK^T and PV at 2 flops per multiply-add each (4 d per
+    visible token and q-head). A leaf's last qpl tokens are its queries;
+    query j sees its ancestors' tokens and the leaf's first L - qpl + 1 + j."""
+    parent = [int(x) for x in inst.parent]
+    lens = [int(x) for x in inst.node_len]
+    n = len(parent)
+    has_child = [False] * n
+    for v in range(n):
+        if parent[v] >= 0:
+            has_child[parent[v]] = True
+    total = 0
+    for v in range(n):
+        if has_child[v]:
+            continue
+        path, u = 0, parent[v]
+        while u >= 0:
+            path += lens[u]
+            u = parent[u]
+        for j in range(inst.qpl):
+            total += path + lens[v] - inst.qpl + 1 + j
+    return total * inst.n_qheads * 4 * inst.head_dim
 
 
 def streamed_kv_bytes(plan, inst):
@@ -416,6 +442,7 @@ def main():
     red_us = float(np.mean(rm)) * 1e3
     dominant = f"partial_kernel<{'bf16' if inst.dtype == torch.bfloat16 else 'f32'},{inst.head_dim}>"
     value = unique / (ms_per_step * 1e-3) / 1e9
+    flops = algorithmic_flops(inst)
     achieved = unique / (part_us * 1e-6) / 1e9
     res = {
         "metric": METRIC,
@@ -456,6 +483,11 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": _traffic(inst.name), "traffic_unit": "bytes per launch",
                      "kernel": dominant, "kernel_us": round(part_us, 3)},
+        "mfma": {"alg_flops": flops, "achieved_tflops": round(flops / (part_us * 1e-6) / 1e12, 1),
+                 "peak_tflops": MFMA_BF16_PEAK_TFLOPS if inst.dtype == torch.bfloat16 else None,
+                 "frac": (round(flops / (part_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+                          if inst.dtype == torch.bfloat16 else None),
+                 "kernel": dominant},
         "graph_us_per_step": round(graph_us, 3) if isinstance(graph_us, float) else graph_us,
         "token_major_pool_us_per_step": round(token_major_us, 2),
         "planner_host_ms": {"tables_median": round(statistics.median(t_host) * 1e3, 3),

@@ -63,3 +63,20 @@ def test_more_than_one_gpu_is_refused():
                          capture_output=True, text=True, timeout=120)
     assert res.returncode == 2
     assert "one GPU" in res.stderr
+
+
+def test_algorithmic_flops_closed_form_and_oracle_counts():
+    """4 d flops per visible token and q-head (QK^T and PV): a hand count on a
+    chain, and on a random tree the oracle's own visible-token counts (the
+    lengths of its softmax weight vectors)."""
+    from oracle import tree_attention as ta
+    b = _bench()
+    # chain root 10 -> leaf 5, two queries per leaf: they see 10 + 4 and 10 + 5 tokens
+    inst = synth.make_tree([-1, 0], [10, 5], page_size=4, qpl=2, n_qheads=2, n_kvheads=1, head_dim=8, seed=1)
+    assert b.algorithmic_flops(inst) == (14 + 15) * 2 * 4 * 8
+    inst = synth.make_tree([-1, 0, 0, 1, 1, 2], [20, 7, 9, 4, 6, 3], page_size=4, qpl=3, n_qheads=4, n_kvheads=2,
+                           head_dim=16, dtype=torch.float32, seed=5)
+    synth.fill_tensors(inst, seed=6)
+    _, w = ta.decode_instance(inst, return_weights=True)
+    visible = sum(len(p) for p in w.values())
+    assert b.algorithmic_flops(inst) == visible * 4 * 16
