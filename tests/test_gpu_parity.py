@@ -66,6 +66,24 @@ def test_workload5_full():
     _check(got, ref, "config 5")
 
 
+@pytest.mark.parametrize("k", [2, 3, 4, 5])
+def test_workload_bench_layout(k):
+    """The full workloads with the pools laid out as bench.py times them
+    (head-major storage, built by bench.py's own helper)."""
+    import importlib.util
+    import os
+    spec = importlib.util.spec_from_file_location(
+        "bench_mod", os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    _log(f"config {k}, head-major pools")
+    inst = synth.make_config(k)
+    dev = (inst.q.cuda(), bench.head_major_pool(inst.k_pool, "cuda"), bench.head_major_pool(inst.v_pool, "cuda"))
+    assert dev[1].stride(1) == inst.head_dim  # tokens of one kv-head's page adjacent
+    got = _run(inst, dev)
+    _check(got, ta.decode_instance(inst), f"config {k} head-major pools")
+
+
 @pytest.mark.parametrize("k", [2, 5])
 def test_plan_invariance(k):
     """Grouping and splitting change only summation order: forced all-0,
