@@ -58,15 +58,13 @@ struct ta_plan {
   void* d_ws = nullptr;  // workspace: o_part | m_part | l_part
   float *d_o_part = nullptr, *d_m_part = nullptr, *d_l_part = nullptr;
   int64_t ws_bytes = 0, ws_cap = 0;
-  // decode-loop updates: pinned host staging (two, alternating; an event marks
-  // when the copy out of each has run) and one device staging buffer
+  // decode-loop updates: pinned host staging (two, alternating), read in place
+  // by the table-scatter kernel; an event marks when that kernel has run
   int32_t* h_stage[2] = {nullptr, nullptr};
   size_t h_stage_cap[2] = {0, 0};
   hipEvent_t stage_done[2] = {nullptr, nullptr};
   bool stage_used[2] = {false, false};
   int32_t stage_next = 0;
-  int32_t* d_stage = nullptr;
-  size_t d_stage_cap = 0;
   bool sized_for_growth = false;  // the first extend gave every region and the workspace headroom
   // 4 per timed decode: start/stop of the partial kernel and of the reduction
   std::vector<hipEvent_t> ev;
@@ -112,11 +110,9 @@ void free_device(ta_plan* p) {
     p->stage_done[x] = nullptr;
     p->h_stage[x] = nullptr;
   }
-  if (p->d_stage) (void)hipFree(p->d_stage);
   if (p->d_tables) (void)hipFree(p->d_tables);
   if (p->d_ws) (void)hipFree(p->d_ws);
   p->d_tables = p->d_ws = nullptr;
-  p->d_stage = nullptr;
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -311,22 +307,8 @@ ta_status upload_incremental(ta_plan* p, hipStream_t s) {
   const size_t words = desc.size() + data.size();
   if (words >= size_t(INT32_MAX)) return set_err(TA_EINVAL, "tree_attn_plan_extend: update too large");
   hipError_t e;
-  // device staging: grown only after the work that may still read it is done
-  if (words > p->d_stage_cap) {
-    if (p->d_stage) {
-      if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_err(e, "tree_attn_plan_extend: hipStreamSynchronize");
-      (void)hipFree(p->d_stage);
-      p->d_stage = nullptr;
-    }
-    const size_t cap = align64w(std::max(2 * words, p->tables_words));
-    if ((e = hipMalloc(&p->d_stage, cap * 4)) != hipSuccess) {
-      p->d_stage = nullptr;
-      p->d_stage_cap = 0;
-      return hip_err(e, "tree_attn_plan_extend: hipMalloc(staging)");
-    }
-    p->d_stage_cap = cap;
-  }
-  // pinned host staging: this buffer's previous copy must have run
+  // pinned host staging, read by the scatter kernel in place: this buffer's
+  // previous scatter must have run
   const int b = p->stage_next;
   if (p->stage_used[b] && (e = hipEventSynchronize(p->stage_done[b])) != hipSuccess)
     return hip_err(e, "tree_attn_plan_extend: hipEventSynchronize");
@@ -346,15 +328,13 @@ ta_status upload_incremental(ta_plan* p, hipStream_t s) {
     return hip_err(e, "tree_attn_plan_extend: hipEventCreate");
   std::memcpy(p->h_stage[b], desc.data(), desc.size() * 4);
   std::memcpy(p->h_stage[b] + desc.size(), data.data(), data.size() * 4);
-  if ((e = hipMemcpyAsync(p->d_stage, p->h_stage[b], words * 4, hipMemcpyHostToDevice, s)) != hipSuccess)
-    return hip_err(e, "tree_attn_plan_extend: hipMemcpyAsync");
+  if ((e = ta::launch_scatter(static_cast<int32_t*>(p->d_tables), int64_t(p->tables_words), p->h_stage[b],
+                              n_desc, s)) != hipSuccess)
+    return hip_err(e, "tree_attn_plan_extend: table update launch");
   if ((e = hipEventRecord(p->stage_done[b], s)) != hipSuccess)
     return hip_err(e, "tree_attn_plan_extend: hipEventRecord");
   p->stage_used[b] = true;
   p->stage_next = b ^ 1;
-  if ((e = ta::launch_scatter(static_cast<int32_t*>(p->d_tables), int64_t(p->tables_words), p->d_stage, n_desc,
-                              s)) != hipSuccess)
-    return hip_err(e, "tree_attn_plan_extend: table update launch");
   return TA_OK;
 }
 

@@ -98,7 +98,9 @@ struct AppendArgs {
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 // Table update: stage holds n_desc descriptors (destination word, words,
 // source word in stage) followed by the words; each range is copied into
-// dst[0, dst_words). The host checks every range lies inside dst.
+// dst[0, dst_words). stage is pinned host memory the kernel reads in place
+// (it must stay unchanged until the kernel has run). The host checks every
+// range lies inside dst.
 hipError_t launch_scatter(int32_t* dst, int64_t dst_words, const int32_t* stage, int32_t n_desc, hipStream_t s);
 
 }  // namespace ta

@@ -1196,7 +1196,8 @@ __global__ __launch_bounds__(kBlock) void lse_reduce_kernel(ReduceArgs a) {
   }
 }
 
-// One workgroup per descriptor (grid-stride over descriptors).
+// One workgroup per descriptor (grid-stride over descriptors); the stage is
+// pinned host memory, read over the bus.
 __global__ void scatter_kernel(int32_t* dst, int64_t dst_words, const int32_t* stage, int32_t n_desc) {
   for (int32_t d = blockIdx.x; d < n_desc; d += gridDim.x) {
     const int64_t to = stage[3 * d], n = stage[3 * d + 1], from = stage[3 * d + 2];
