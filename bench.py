@@ -207,10 +207,11 @@ def _decode_loop(args, inst, dev):
     extend, the same decodes without growth, and the host time of planning
     the grown tree from scratch (what each step would cost without reuse).
     Each step first writes the new tokens' K/V into the pools with
-    tree_attn_kv_append (fixed rows: this mode times, it does not check)."""
+    tree_attn_kv_append (a prepared appender; fixed rows: this mode times, it
+    does not check)."""
     import numpy as np
     import torch
-    from tree_structured_shared_amd import Plan, kv_append
+    from tree_structured_shared_amd import Plan, kv_appender
     K, W = args.steps, args.warmup
     ps, qpl = inst.page_size, inst.qpl
     has_child = np.zeros(inst.n_nodes, bool)
@@ -245,9 +246,10 @@ def _decode_loop(args, inst, dev):
     plan = Plan.for_instance(inst)
     stream = torch.cuda.current_stream(dev).cuda_stream
     call = plan.launcher(q, k, v, out, stream)
+    append = kv_appender(k, v, k_new, v_new, stream)
     add = np.full(len(leaves), qpl, np.int32)
     for s in range(W):
-        kv_append(k, v, k_new, v_new, dsts[s], stream)
+        append(dsts[s])
         plan.extend(add, sched[s], stream)
         call()
     torch.cuda.synchronize()
@@ -255,7 +257,7 @@ def _decode_loop(args, inst, dev):
     gc.disable()
     t0 = time.perf_counter()
     for s in range(W, W + K):
-        kv_append(k, v, k_new, v_new, dsts[s], stream)
+        append(dsts[s])
         a = time.perf_counter()
         relaunches += int(plan.extend(add, sched[s], stream))
         t_ext.append(time.perf_counter() - a)

@@ -152,6 +152,32 @@ def test_kv_append_scatter(dtype, d):
     assert torch.equal(kd.cpu(), want_k) and torch.equal(vd.cpu(), want_v)
 
 
+def test_kv_appender_reuses_buffers():
+    """A prepared appender writes each call's rows where that call's dst
+    says (same result as kv_append), and checks dst on every call."""
+    from tree_structured_shared_amd import TreeAttnError, kv_append, kv_appender
+    g = torch.Generator().manual_seed(7)
+    n_pages, ps, h, d, n = 24, 16, 2, 128, 40
+    k_pool = torch.randn((n_pages, ps, h, d), generator=g).to(torch.bfloat16)
+    v_pool = torch.randn((n_pages, ps, h, d), generator=g).to(torch.bfloat16)
+    k_new = torch.randn((n, h, d), generator=g).to(torch.bfloat16).cuda()
+    v_new = torch.randn((n, h, d), generator=g).to(torch.bfloat16).cuda()
+    cells = torch.randperm(n_pages * ps, generator=g)[:2 * n]
+    dsts = [((cells[x * n:(x + 1) * n] // ps) << 8 | cells[x * n:(x + 1) * n] % ps).to(torch.int32).cuda()
+            for x in range(2)]
+    ka, va = k_pool.cuda(), v_pool.cuda()
+    kb, vb = k_pool.cuda(), v_pool.cuda()
+    app = kv_appender(ka, va, k_new, v_new)
+    for dst in dsts:
+        app(dst)
+        kv_append(kb, vb, k_new, v_new, dst)
+    torch.cuda.synchronize()
+    assert torch.equal(ka, kb) and torch.equal(va, vb)
+    assert not torch.equal(ka.cpu(), k_pool)
+    with pytest.raises(TreeAttnError):
+        app(dsts[0].to(torch.int64))
+
+
 def test_decode_loop_append_extend_decode():
     """A decode loop through the library only: the new tokens' K/V go in with
     kv_append, the plan grows with extend, the decode matches the oracle on

@@ -161,3 +161,14 @@ def test_kv_append_argument_errors():
                         stride_token=4 * 128, stride_head=100)
     assert call(ctypes.byref(bad)) == _capi.TA_EINVAL                      # stride not 16-byte
     assert call(ctypes.byref(kv), n=0) == _capi.TA_OK                      # nothing to do
+
+
+def test_kv_appender_rejects_host_pools():
+    """Host tensors never reach the kernel: the binding refuses them before
+    any HIP call."""
+    import torch
+    from tree_structured_shared_amd import kv_appender
+    pool = torch.zeros((4, 16, 2, 64), dtype=torch.bfloat16)
+    rows = torch.zeros((3, 2, 64), dtype=torch.bfloat16)
+    with pytest.raises(TreeAttnError):
+        kv_appender(pool, pool.clone(), rows, rows.clone())

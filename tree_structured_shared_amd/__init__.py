@@ -18,7 +18,7 @@ import numpy as np
 from ._capi import (TA_BF16, TA_F32, TABLE_COLS, TABLE_IDS, PagedKV, PlanOpts, TreeAttnError,
                     check, lib)
 
-__all__ = ["Plan", "TreeAttnError", "TABLE_IDS", "kv_append"]
+__all__ = ["Plan", "TreeAttnError", "TABLE_IDS", "kv_append", "kv_appender"]
 
 
 def _i32(a):
@@ -26,23 +26,33 @@ def _i32(a):
     return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
 
 
-def kv_append(k_pool, v_pool, k_new, v_new, dst, stream=None):
-    """Write the new tokens' K/V rows into the paged pools
-    (tree_attn_kv_append): token r's rows k_new[r] / v_new[r]
-    ([n_kvheads, head_dim]) go to page dst[r] >> 8, slot dst[r] & 255; dst is a
-    device int32 tensor. Destinations outside the pools are skipped."""
+def _i32_addr(a):
+    """(array, address) of a contiguous int32 version of a; no copy (and no
+    ctypes object) when a already is one."""
+    if not (isinstance(a, np.ndarray) and a.dtype == np.int32 and a.flags.c_contiguous):
+        a = np.ascontiguousarray(np.asarray(a), dtype=np.int32)
+    return a, a.__array_interface__["data"][0]
+
+
+def kv_appender(k_pool, v_pool, k_new, v_new, stream=None):
+    """Check the pools and the new-row buffers once and return a callable
+    append(dst) that enqueues tree_attn_kv_append for them (for loops that
+    append into the same buffers every step): token r's rows k_new[r] /
+    v_new[r] ([n_kvheads, head_dim]) go to page dst[r] >> 8, slot dst[r] &
+    255; dst is a device int32 [n_tokens] tensor, checked per call.
+    Destinations outside the pools are skipped."""
     import torch
     dt = {torch.float32: TA_F32, torch.bfloat16: TA_BF16}.get(k_pool.dtype)
     if dt is None:
         raise TreeAttnError(4, f"unsupported dtype {k_pool.dtype}")
     if k_pool.dim() != 4 or k_pool.shape != v_pool.shape or k_pool.stride() != v_pool.stride():
         raise TreeAttnError(1, "pools must be [n_pages, page_size, n_kvheads, head_dim] with equal strides")
+    if not (k_pool.is_cuda and v_pool.is_cuda) or v_pool.dtype != k_pool.dtype:
+        raise TreeAttnError(1, "pools must be device tensors of one dtype")
     n, h, d = k_new.shape[0], k_pool.shape[2], k_pool.shape[3]
     for name, t in (("k_new", k_new), ("v_new", v_new)):
         if tuple(t.shape) != (n, h, d) or t.dtype != k_pool.dtype or not t.is_contiguous() or not t.is_cuda:
             raise TreeAttnError(1, f"{name} must be a contiguous device [n_tokens, {h}, {d}] {k_pool.dtype} tensor")
-    if (dst.dtype != torch.int32 or tuple(dst.shape) != (n,) or not dst.is_contiguous() or not dst.is_cuda):
-        raise TreeAttnError(1, "dst must be a contiguous device int32 [n_tokens] tensor")
     if k_pool.stride(3) != 1:
         raise TreeAttnError(1, "head_dim must be contiguous in the pools")
     kv = PagedKV(k=k_pool.data_ptr(), v=v_pool.data_ptr(), dtype=dt, page_size=k_pool.shape[1],
@@ -50,9 +60,26 @@ def kv_append(k_pool, v_pool, k_new, v_new, dst, stream=None):
                  stride_head=k_pool.stride(2))
     if stream is None:
         stream = torch.cuda.current_stream(k_pool.device).cuda_stream
-    check(lib().tree_attn_kv_append(ctypes.byref(kv), ctypes.c_void_p(k_new.data_ptr()),
-                                    ctypes.c_void_p(v_new.data_ptr()), int(n), int(h), int(d),
-                                    ctypes.c_void_p(dst.data_ptr()), ctypes.c_void_p(stream)))
+    fn = lib().tree_attn_kv_append
+    head = (ctypes.byref(kv), ctypes.c_void_p(k_new.data_ptr()), ctypes.c_void_p(v_new.data_ptr()),
+            int(n), int(h), int(d))
+    tail = ctypes.c_void_p(stream)
+    keep = (kv, k_pool, v_pool, k_new, v_new)
+    i32 = torch.int32
+
+    def append(dst, _fn=fn, _head=head, _tail=tail, _keep=keep):
+        if dst.dtype != i32 or dst.shape != (n,) or not dst.is_cuda or not dst.is_contiguous():
+            raise TreeAttnError(1, "dst must be a contiguous device int32 [n_tokens] tensor")
+        check(_fn(*_head, ctypes.c_void_p(dst.data_ptr()), _tail))
+    return append
+
+
+def kv_append(k_pool, v_pool, k_new, v_new, dst, stream=None):
+    """One tree_attn_kv_append (see kv_appender): token r's rows k_new[r] /
+    v_new[r] ([n_kvheads, head_dim]) go to page dst[r] >> 8, slot dst[r] &
+    255; dst is a device int32 tensor. Destinations outside the pools are
+    skipped."""
+    kv_appender(k_pool, v_pool, k_new, v_new, stream)(dst)
 
 
 class Plan:
@@ -130,16 +157,16 @@ class Plan:
         the grouping is kept (tree_attn_plan_extend). Returns True when a
         captured decode graph must be captured again."""
         n_leaves = self.n_queries // self.qpl
-        add, add_p = _i32(leaf_add)
-        pages, pages_p = _i32(new_pages)
+        add, add_a = _i32_addr(leaf_add)
+        pages, pages_a = _i32_addr(new_pages)
         if len(add) != n_leaves:
             raise TreeAttnError(1, f"leaf_add must have one entry per leaf ({n_leaves})")
         if stream is None and not self.host_only:
             import torch
             stream = torch.cuda.current_stream().cuda_stream
         relaunch = ctypes.c_int32()
-        check(lib().tree_attn_plan_extend(self._handle, add_p, pages_p if len(pages) else None, len(pages),
-                                          ctypes.c_void_p(stream or 0), ctypes.byref(relaunch)))
+        check(lib().tree_attn_plan_extend(self._handle, add_a, pages_a if len(pages) else None, len(pages),
+                                          stream or None, ctypes.byref(relaunch)))
         if relaunch.value or self.host_only:
             self._info()
         return bool(relaunch.value)

@@ -71,7 +71,9 @@ def lib():
     L.tree_attn_decode.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(PagedKV),
                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     L.tree_attn_decode.restype = ctypes.c_int
-    L.tree_attn_plan_extend.argtypes = [ctypes.c_void_p, i32p, i32p, ctypes.c_int64, ctypes.c_void_p, i32p]
+    # leaf_add and new_pages are passed as addresses (int32 arrays)
+    L.tree_attn_plan_extend.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                        ctypes.c_void_p, i32p]
     L.tree_attn_plan_extend.restype = ctypes.c_int
     L.tree_attn_kv_append.argtypes = [ctypes.POINTER(PagedKV), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
