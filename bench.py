@@ -299,7 +299,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--copies", type=int, default=0, help="KV pool copies (0 = enough for 1 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
