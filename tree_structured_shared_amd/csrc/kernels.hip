@@ -29,8 +29,8 @@
 //    tiles (padded for fewer rows: the items are bound by their K/V stream).
 //    S^T = K Q^T: K rows are the A operand (straight from the pool, or from
 //    LDS). O^T = V^T P^T: the score accumulators already sit in the B-operand
-//    layout of P^T; V^T comes from a v_perm transpose of 16-byte V reads, or
-//    in workgroup waves with two row tiles from LDS transpose reads
+//    layout of P^T; V^T comes from a v_perm transpose of 16-byte V reads
+//    (single-wave items) or from LDS transpose reads (workgroup items)
 //    (stacking the queries that share KV turns the decode GEMV into a GEMM,
 //    FastTree review, kernel design).
 //  * fp32: wavefront dot products (GEMV), 8 lanes per token, DPP reductions,
@@ -808,8 +808,7 @@ struct TileDma {
 
 // One tile for the wave's first NACT row tiles, operands read straight from
 // an LDS stage: K one k-step at a time (the A operand of S^T for both token
-// blocks), then the eight V token slices (16 lanes of a row group read one
-// token's 16 chunks: distinct banks) and V^T two d-blocks at a time.
+// blocks), then V^T one 16-wide d-block at a time by transpose reads.
 template <int D, int NRTW, int NACT, bool HILO>
 __device__ __forceinline__ void lds_tile(MfmaState<D, NRTW>& S, const char* stage, const PartialArgs& a,
                                          const WorkItem& it, int base, int i, int j) {
@@ -832,57 +831,28 @@ __device__ __forceinline__ void lds_tile(MfmaState<D, NRTW>& S, const char* stag
 #pragma unroll
   for (int k = 0; k < NACT; ++k)
     mfma_softmax<D, NRTW, HILO, true>(S, k, s0[k], s1[k], a, it, base, j, pb[k], pl[k]);
-  if constexpr (NACT == 2) {
-    // V^T operands by LDS transpose reads: within each 16-lane group, lane L of
-    // a ds_read_b64_tr_b16 receives element k = the (L % 4)-th 16-bit value at
-    // the address of lane 4k + L / 4. Lane (i, j) points at token
-    // 16 r + 4 j + i / 4, d = 16 db + 4 (i % 4): it gets d = 16 db + i of tokens
-    // 16 r + 4 j + k, k = 0..3 -- with r = 0, 1 the token order tau(j, e) of P.
-    typedef short v4s __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(3))) v4s lds_v4s;
-    typedef __attribute__((address_space(3))) char lds_b;
-    const lds_b* vstage = (const lds_b*)stage + L::PART;
+  // V^T operands by LDS transpose reads: within each 16-lane group, lane L of
+  // a ds_read_b64_tr_b16 receives element k = the (L % 4)-th 16-bit value at
+  // the address of lane 4k + L / 4. Lane (i, j) points at token
+  // 16 r + 4 j + i / 4, d = 16 db + 4 (i % 4): it gets d = 16 db + i of tokens
+  // 16 r + 4 j + k, k = 0..3 -- with r = 0, 1 the token order tau(j, e) of P.
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4s lds_v4s;
+  typedef __attribute__((address_space(3))) char lds_b;
+  const lds_b* vstage = (const lds_b*)stage + L::PART;
 #pragma unroll
-    for (int db = 0; db < DPL; ++db) {
-      v4s half[2];
+  for (int db = 0; db < DPL; ++db) {
+    v4s half[2];
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int t = 16 * r + 4 * j + (i >> 2);
-        const int c = 2 * db + ((i & 3) >> 1);
-        half[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4s*)(vstage + t * L::ROW + ((c ^ (t & (L::CH - 1))) << 4) + 8 * (i & 1)));
-      }
-      const bf16x8 vt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-      for (int k = 0; k < NACT; ++k) pv_update<D, NRTW, HILO>(S, k, db, vt, pb[k], pl[k]);
+    for (int r = 0; r < 2; ++r) {
+      const int t = 16 * r + 4 * j + (i >> 2);
+      const int c = 2 * db + ((i & 3) >> 1);
+      half[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4s*)(vstage + t * L::ROW + ((c ^ (t & (L::CH - 1))) << 4) + 8 * (i & 1)));
     }
-  } else {  // one row tile: v_perm from two 16-byte reads per token is the shorter chain
-    VSlice<DPL> vs[8];
+    const bf16x8 vt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int t = tau(j, e);
-      if constexpr (D == 128) {
-        vs[e].w = *reinterpret_cast<const u32x4*>(stage + L::off(1, t, i));
-      } else {
-        vs[e].w = *reinterpret_cast<const u32x2*>(stage + L::off(1, t, i >> 1) + (i & 1) * 8);
-      }
-    }
-    // word w of a token's V slice holds d-blocks 2w (low halves) and 2w + 1
-#pragma unroll
-    for (int w = 0; w < DPL / 2; ++w) {
-      u32x4 lo, hi;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        lo[u] = __builtin_amdgcn_perm(vs[2 * u + 1].word(w), vs[2 * u].word(w), 0x05040100u);
-        hi[u] = __builtin_amdgcn_perm(vs[2 * u + 1].word(w), vs[2 * u].word(w), 0x07060302u);
-      }
-      const bf16x8 vlo = __builtin_bit_cast(bf16x8, lo), vhi = __builtin_bit_cast(bf16x8, hi);
-#pragma unroll
-      for (int k = 0; k < NACT; ++k) {
-        pv_update<D, NRTW, HILO>(S, k, 2 * w, vlo, pb[k], pl[k]);
-        pv_update<D, NRTW, HILO>(S, k, 2 * w + 1, vhi, pb[k], pl[k]);
-      }
-    }
+    for (int k = 0; k < NACT; ++k) pv_update<D, NRTW, HILO>(S, k, db, vt, pb[k], pl[k]);
   }
   // l = ones x P^T: the row sums of the weights the P V product used, summed
   // on the matrix cores in fp32 (the VALU sum they replace is 16 converts
@@ -1037,10 +1007,8 @@ __device__ __forceinline__ void block_lds_item(const PartialArgs& a, char* lds, 
     } else {
       lds_stream<D, FA, 0, false>(S, lds, a, it, h, i, j);
     }
-    // waves with two row tiles built V^T by transpose reads (d = 16 db + 4j + c);
-    // every workgroup wave summed l on the matrix cores
-    if (S.on[1]) mfma_write<D, kBlockRowTiles, true>(S, a);
-    else mfma_write<D, kBlockRowTiles, false, true>(S, a);
+    // V^T came from transpose reads (d = 16 db + 4j + c), l from the matrix cores
+    mfma_write<D, kBlockRowTiles, true>(S, a);
   }
 }
 
