@@ -946,14 +946,16 @@ __device__ __forceinline__ void lds_stream(MfmaState<D, kBlockRowTiles>& S, char
     dma.issue(lds + t * ST, e[t], a);
     dma4(st, word_off(t + AHEAD), lds_addr(t * ST + wpos));
   }
-  int stage = 0;
-  for (int n = 0; n < ntiles; ++n) {
+  // one tile in stage SG (a compile-time stage, so every LDS address below is
+  // a loop-invariant lane offset plus an immediate)
+  auto step = [&](int n, auto sg) {
+    constexpr int SG = decltype(sg)::value;
     // this wave's loads of tile n (and the words of tile n + AHEAD) landed;
     // those of the next AHEAD - 1 tiles in flight
     lds_stage_barrier<(AHEAD - 1) * (NIW + 1)>();
     int32_t w[NIW];
     {
-      const char* wp = lds + stage * ST + rpos;
+      const char* wp = lds + SG * ST + rpos;
       if constexpr (NIW == 4) {
         const i32x4 w4 = *reinterpret_cast<const i32x4*>(wp);
 #pragma unroll
@@ -963,12 +965,18 @@ __device__ __forceinline__ void lds_stream(MfmaState<D, kBlockRowTiles>& S, char
         for (int x = 0; x < NIW; ++x) w[x] = reinterpret_cast<const int32_t*>(wp)[x];
       }
     }
-    const int sf = stage == 0 ? NS - 1 : stage - 1;  // the stage of tile n - 1, done by every wave
-    dma.issue(lds + sf * ST, w, a);
-    dma4(st, word_off(n + 2 * AHEAD), lds_addr(sf * ST + wpos));
+    constexpr int SF = SG == 0 ? NS - 1 : SG - 1;  // the stage of tile n - 1, done by every wave
+    dma.issue(lds + SF * ST, w, a);
+    dma4(st, word_off(n + 2 * AHEAD), lds_addr(SF * ST + wpos));
     if constexpr (NACT > 0)
-      lds_tile<D, kBlockRowTiles, NACT, HILO>(S, lds + stage * ST, a, it, it.tok0 + n * 32, i, j);
-    stage = stage + 1 == NS ? 0 : stage + 1;
+      lds_tile<D, kBlockRowTiles, NACT, HILO>(S, lds + SG * ST, a, it, it.tok0 + n * 32, i, j);
+  };
+  static_assert(NS == 3, "the loop is unrolled over three stages");
+  // wave-uniform: tile n sits in stage n mod 3
+  for (int n = 0; n < ntiles; n += NS) {
+    step(n, std::integral_constant<int, 0>());
+    if (n + 1 < ntiles) step(n + 1, std::integral_constant<int, 1>());
+    if (n + 2 < ntiles) step(n + 2, std::integral_constant<int, 2>());
   }
   // every wave's direct loads (the clamped ones past the end included) land
   // before the stages are reused
