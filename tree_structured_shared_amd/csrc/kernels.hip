@@ -703,7 +703,13 @@ __device__ __forceinline__ void mfma_wave(const PartialArgs& a, const WorkItem& 
 // direct-to-LDS loads into one of kLdsStages stages (two tiles in flight while
 // one is computed), and one barrier per tile hands a stage over. Token rows
 // are stored with their 16-byte chunks XOR-swizzled by the token index, so the
-// MFMA operand reads (16 lanes = 16 tokens or 16 chunks) hit distinct banks.
+// MFMA operand reads hit distinct banks. K rows are read 16 tokens x one
+// chunk at a time: chunk c of token t sits at c ^ t. V rows are read by
+// transpose reads, 8 tokens x 2 adjacent chunks per half wave: at 16 chunks
+// a row (D = 128) chunk c of token t sits at c ^ 2t, which maps those 16
+// pieces to 16 distinct 16-byte positions of a row (c ^ t would put token t,
+// chunk 2b and token t ^ 1, chunk 2b + 1 on the same banks); at 8 chunks a
+// row two tokens share a 256-byte bank line and c ^ t already spreads them.
 // A stage ends in each wave's page-table words for the tile two later.
 template <int D>
 struct LdsTile {
@@ -712,8 +718,12 @@ struct LdsTile {
   static constexpr int PART = 32 * ROW;    // one K or V tile
   static constexpr int WORDS = 256;        // per wave: the page-table words of a later tile
   static constexpr int STAGE = 2 * PART + kWaves * WORDS;  // K, V, then the words
+  // XOR applied to the chunk index of token t's row in part 0 (K) or 1 (V)
+  static __device__ __forceinline__ int swz(int part, int t) {
+    return (CH == 16 ? t << part : t) & (CH - 1);
+  }
   static __device__ __forceinline__ int off(int part, int t, int c) {
-    return part * PART + t * ROW + ((c ^ (t & (CH - 1))) << 4);
+    return part * PART + t * ROW + ((c ^ swz(part, t)) << 4);
   }
 };
 
@@ -765,8 +775,8 @@ __device__ __forceinline__ void dma4(const int32_t* base, uint32_t off, uint32_t
 // instruction fills 1 KiB = RPK token rows. A tile's K and V take NI
 // instructions, NIW per wave. Lane l of an instruction covers token
 // t = blk * RPK + l / CH at LDS chunk position p = l % CH and fetches the
-// global chunk p ^ (t mod CH): the same XOR swizzle as LdsTile::off, with no
-// register staging.
+// global chunk p ^ LdsTile::swz(part, t): the swizzle of LdsTile::off, with
+// no register staging.
 template <int D, bool FA>
 struct TileDma {
   typedef LdsTile<D> L;
@@ -798,7 +808,7 @@ struct TileDma {
       const int part = m / (NI / 2), blk = m % (NI / 2);
       const int32_t sg = e[x];
       const int t = blk * RPK + r;
-      const Off off = TokOff<FA>::of(sg, a) + Off(((p ^ (t & (CH - 1))) << 4));
+      const Off off = TokOff<FA>::of(sg, a) + Off(((p ^ L::swz(part, t)) << 4));
       const uint32_t dst = __builtin_amdgcn_readfirstlane(
           uint32_t(reinterpret_cast<uintptr_t>((lds_char*)(stage + part * L::PART + blk * 1024))));
       dma16(part ? vb : kb, off, dst);
@@ -848,7 +858,7 @@ __device__ __forceinline__ void lds_tile(MfmaState<D, NRTW>& S, const char* stag
       const int t = 16 * r + 4 * j + (i >> 2);
       const int c = 2 * db + ((i & 3) >> 1);
       half[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_v4s*)(vstage + t * L::ROW + ((c ^ (t & (L::CH - 1))) << 4) + 8 * (i & 1)));
+          (lds_v4s*)(vstage + t * L::ROW + ((c ^ L::swz(1, t)) << 4) + 8 * (i & 1)));
     }
     const bf16x8 vt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
