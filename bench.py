@@ -208,7 +208,9 @@ def _decode_loop(args, inst, dev):
     the grown tree from scratch (what each step would cost without reuse).
     Each step first writes the new tokens' K/V into the pools with
     tree_attn_kv_append (a prepared appender; fixed rows: this mode times, it
-    does not check)."""
+    does not check); the same loop is also timed, from a fresh plan and
+    fresh pools, with tree_attn_plan_extend_append (append and table update
+    in one launch). Extend host times are those of the separate calls."""
     import numpy as np
     import torch
     from tree_structured_shared_amd import Plan, kv_appender
@@ -234,36 +236,52 @@ def _decode_loop(args, inst, dev):
         sched.append(np.asarray(pages, np.int32))
         dsts.append(torch.tensor(locs, dtype=torch.int32, device=dev))
     shape = (next_page,) + tuple(inst.k_pool.shape[1:])
-    k = torch.zeros(shape, dtype=inst.dtype, device=dev)
-    v = torch.zeros(shape, dtype=inst.dtype, device=dev)
-    k[:inst.n_pages].copy_(inst.k_pool)
-    v[:inst.n_pages].copy_(inst.v_pool)
     q = inst.q.to(dev)
     out = torch.empty((inst.n_queries, inst.n_qheads, inst.head_dim), dtype=torch.float32, device=dev)
     new_rows = len(leaves) * qpl
     k_new = torch.randn((new_rows, inst.n_kvheads, inst.head_dim), device=dev).to(inst.dtype)
     v_new = torch.randn((new_rows, inst.n_kvheads, inst.head_dim), device=dev).to(inst.dtype)
-    plan = Plan.for_instance(inst)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    call = plan.launcher(q, k, v, out, stream)
-    append = kv_appender(k, v, k_new, v_new, stream)
     add = np.full(len(leaves), qpl, np.int32)
-    for s in range(W):
-        append(dsts[s])
-        plan.extend(add, sched[s], stream)
-        call()
-    torch.cuda.synchronize()
-    t_ext, relaunches = [], 0
+
+    def loop(fused):
+        # W + K steps from the original tree: fresh pools and plan
+        k = torch.zeros(shape, dtype=inst.dtype, device=dev)
+        v = torch.zeros(shape, dtype=inst.dtype, device=dev)
+        k[:inst.n_pages].copy_(inst.k_pool)
+        v[:inst.n_pages].copy_(inst.v_pool)
+        plan = Plan.for_instance(inst)
+        call = plan.launcher(q, k, v, out, stream)
+        append = kv_appender(k, v, k_new, v_new, stream)
+
+        def step(s):
+            if fused:
+                return int(plan.extend(add, sched[s], stream, append=(append, dsts[s])))
+            append(dsts[s])
+            return int(plan.extend(add, sched[s], stream))
+        for s in range(W):
+            step(s)
+            call()
+        torch.cuda.synchronize()
+        t_ext, relaunches = [], 0
+        gc.disable()
+        t0 = time.perf_counter()
+        for s in range(W, W + K):
+            a = time.perf_counter()
+            relaunches += step(s)
+            t_ext.append(time.perf_counter() - a)
+            call()
+        torch.cuda.synchronize()
+        loop_us = (time.perf_counter() - t0) * 1e6 / K
+        gc.enable()
+        return loop_us, t_ext, relaunches, plan, call
+
+    fused = loop(True)
+    fused_us = fused[0]
+    fused[3].close()
+    del fused
+    loop_us, t_ext, relaunches, plan, call = loop(False)
     gc.disable()
-    t0 = time.perf_counter()
-    for s in range(W, W + K):
-        append(dsts[s])
-        a = time.perf_counter()
-        relaunches += int(plan.extend(add, sched[s], stream))
-        t_ext.append(time.perf_counter() - a)
-        call()
-    torch.cuda.synchronize()
-    loop_us = (time.perf_counter() - t0) * 1e6 / K
     t0 = time.perf_counter()
     for s in range(K):
         call()
@@ -284,6 +302,7 @@ def _decode_loop(args, inst, dev):
     P = plan.export("params")
     print(json.dumps({"decode_loop": inst.name, "steps": K, "warmup": W, "tokens_per_leaf_per_step": qpl,
                       "us_per_step_append_extend_decode": round(loop_us, 2),
+                      "us_per_step_fused_append_extend_decode": round(fused_us, 2),
                       "us_per_step_no_growth": round(static_us, 2),
                       "extend_host_us_median": round(statistics.median(t_ext) * 1e6, 2),
                       "extend_host_us_p90": round(sorted(t_ext)[int(0.9 * (len(t_ext) - 1))] * 1e6, 2),

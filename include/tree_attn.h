@@ -160,6 +160,23 @@ ta_status tree_attn_plan_extend(ta_plan* plan, const int32_t* leaf_add, const in
 ta_status tree_attn_kv_append(const ta_paged_kv* kv, const void* k_new, const void* v_new, int64_t n_tokens,
                               int32_t n_kvheads, int32_t head_dim, const int32_t* dst, void* hip_stream);
 
+/* One decode-loop step's two device updates in one call (plan reuse, as for
+ * tree_attn_plan_extend: FastTree review, section 3.2): the KV append of
+ * tree_attn_kv_append(kv, k_new, v_new, n_tokens, the plan's n_kvheads, the
+ * plan's head_dim, dst) and the plan growth of tree_attn_plan_extend(plan,
+ * leaf_add, new_pages, n_new_pages). When the tables are updated in place
+ * (every extend after the first, until they outgrow their headroom) both
+ * updates go to hip_stream as ONE kernel launch instead of two; otherwise the
+ * append is enqueued after the table upload. Results equal the two calls'.
+ * Arguments, ownership and asynchrony as in those calls; kv->page_size must be
+ * the plan's. The append's arguments are checked before the plan changes, so
+ * TA_EINVAL / TA_EUNSUPPORTED from either part leave pools and plan
+ * untouched. host_only plans: TA_EINVAL. n_tokens == 0 extends only. */
+ta_status tree_attn_plan_extend_append(ta_plan* plan, const int32_t* leaf_add, const int32_t* new_pages,
+                                       int64_t n_new_pages, const ta_paged_kv* kv, const void* k_new,
+                                       const void* v_new, int64_t n_tokens, const int32_t* dst, void* hip_stream,
+                                       int32_t* relaunch);
+
 /* Plan sizes. Any output pointer may be NULL. */
 ta_status tree_attn_plan_info(const ta_plan* plan, int32_t* n_queries, int64_t* workspace_bytes,
                               int32_t* n_items);

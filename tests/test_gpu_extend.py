@@ -215,3 +215,62 @@ def test_decode_loop_append_extend_decode():
         assert torch.equal(vd[:grown.n_pages].cpu(), grown.v_pool)
         inst = grown
     plan.close()
+
+
+def test_fused_append_extend_matches_separate_calls():
+    """tree_attn_plan_extend_append (one launch for the KV append and the
+    table update) against tree_attn_kv_append + tree_attn_plan_extend on a
+    twin plan and twin pools: the same pools, tables and (bit-identical)
+    decode outputs every step, within the tolerance of the oracle; covers the
+    first extend (tables uploaded whole), in-place updates, a step that
+    outgrows a leaf's page-table slack and a step with no new tokens."""
+    from tree_structured_shared_amd import kv_append, kv_appender
+    inst = _small_tree(torch.bfloat16, 2)
+    spare = 96
+    pools = []
+    for _ in range(2):
+        kd = torch.zeros((inst.n_pages + spare,) + tuple(inst.k_pool.shape[1:]), dtype=inst.dtype, device="cuda")
+        vd = torch.full(kd.shape, synth.CANARY_V, dtype=torch.float32, device="cuda").to(inst.dtype)
+        kd[:inst.n_pages].copy_(inst.k_pool)
+        vd[:inst.n_pages].copy_(inst.v_pool)
+        pools.append((kd, vd))
+    plans = [Plan.for_instance(inst, poison_workspace=True) for _ in range(2)]
+    has_child = np.zeros(inst.n_nodes, bool)
+    has_child[inst.parent[inst.parent >= 0]] = True
+    leaves = np.flatnonzero(~has_child)
+    for step, extra in enumerate([0, 0, 300, 0, -1, 0]):
+        add = np.zeros(inst.n_leaves, np.int64) if extra < 0 else np.full(inst.n_leaves, inst.qpl) + extra
+        grown, new_pages = synth.grow_leaves(inst, add, seed=700 + step)
+        assert grown.n_pages <= pools[0][0].shape[0]
+        locs, rows_k, rows_v = [], [], []
+        for v in leaves:
+            pages = grown.node_page_ids[grown.node_page_ptr[v]:grown.node_page_ptr[v + 1]]
+            for t in range(int(inst.node_len[v]), int(grown.node_len[v])):
+                pg, sl = int(pages[t // grown.page_size]), t % grown.page_size
+                locs.append((pg << 8) | sl)
+                rows_k.append(grown.k_pool[pg, sl])
+                rows_v.append(grown.v_pool[pg, sl])
+        shape = (len(locs), inst.n_kvheads, inst.head_dim)
+        k_new = torch.stack(rows_k).cuda().contiguous() if locs else torch.zeros(shape, dtype=inst.dtype, device="cuda")
+        v_new = torch.stack(rows_v).cuda().contiguous() if locs else torch.zeros(shape, dtype=inst.dtype, device="cuda")
+        dst = torch.tensor(locs, dtype=torch.int32, device="cuda")
+        _log(f"fused append+extend step {step}: {len(locs)} new tokens")
+        (ka, va), (kb, vb) = pools
+        kv_append(ka, va, k_new, v_new, dst)
+        ra = plans[0].extend(add, new_pages)
+        rb = plans[1].extend(add, new_pages, append=(kv_appender(kb, vb, k_new, v_new), dst))
+        assert ra == rb
+        outs = [p.decode(grown.q.cuda(), k, v) for p, (k, v) in zip(plans, pools)]
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0], outs[1]), f"step {step}: fused and separate outputs differ"
+        _check(outs[1], ta.decode_instance(grown), f"fused append+extend step {step}")
+        ta_, tb_ = plans[0].tables(), plans[1].tables()
+        assert ta_.keys() == tb_.keys()
+        for name in ta_:
+            assert np.array_equal(ta_[name], tb_[name]), (step, name)
+        assert torch.equal(kb, ka) and torch.equal(vb, va)
+        assert torch.equal(kb[:grown.n_pages].cpu(), grown.k_pool)
+        assert torch.equal(vb[:grown.n_pages].cpu(), grown.v_pool)
+        inst = grown
+    for p in plans:
+        p.close()

@@ -172,3 +172,20 @@ def test_kv_appender_rejects_host_pools():
     rows = torch.zeros((3, 2, 64), dtype=torch.bfloat16)
     with pytest.raises(TreeAttnError):
         kv_appender(pool, pool.clone(), rows, rows.clone())
+
+
+def test_extend_append_argument_errors():
+    """tree_attn_plan_extend_append refuses a NULL plan and a host-only plan
+    before any HIP call, and leaves the plan as it was."""
+    L = _capi.lib()
+    kv = _capi.PagedKV(k=256, v=512, dtype=_capi.TA_BF16, page_size=16, n_pages=4, stride_page=16 * 4 * 128,
+                       stride_token=4 * 128, stride_head=128)
+    add = (ctypes.c_int32 * 1)(1)
+    assert L.tree_attn_plan_extend_append(None, add, None, 0, ctypes.byref(kv), 1024, 2048, 1, 4096, None,
+                                          None) == _capi.TA_EINVAL
+    p = Plan([-1, 0], [4, 4], [0, 1, 2], [0, 1], 16, 1, 4, 4, 128, host_only=True)
+    before = p.export("params").copy()
+    assert L.tree_attn_plan_extend_append(p._handle, add, None, 0, ctypes.byref(kv), 1024, 2048, 1, 4096, None,
+                                          None) == _capi.TA_EINVAL
+    assert np.array_equal(p.export("params"), before)
+    p.close()

@@ -71,6 +71,15 @@ def kv_appender(k_pool, v_pool, k_new, v_new, stream=None):
         if dst.dtype != i32 or dst.shape != (n,) or not dst.is_cuda or not dst.is_contiguous():
             raise TreeAttnError(1, "dst must be a contiguous device int32 [n_tokens] tensor")
         check(_fn(*_head, ctypes.c_void_p(dst.data_ptr()), _tail))
+
+    def fused_args(dst, _kv=kv, _keep=keep):
+        # the append's half of tree_attn_plan_extend_append's arguments
+        if dst.dtype != i32 or dst.shape != (n,) or not dst.is_cuda or not dst.is_contiguous():
+            raise TreeAttnError(1, "dst must be a contiguous device int32 [n_tokens] tensor")
+        return (ctypes.byref(_kv), ctypes.c_void_p(k_new.data_ptr()), ctypes.c_void_p(v_new.data_ptr()), int(n),
+                ctypes.c_void_p(dst.data_ptr()))
+    append.fused_args = fused_args
+    append.stream = stream
     return append
 
 
@@ -151,22 +160,33 @@ class Plan:
         return {k: self.export(k) for k in TABLE_IDS}
 
     # -- decode loop ----------------------------------------------------------
-    def extend(self, leaf_add, new_pages=(), stream=None):
+    def extend(self, leaf_add, new_pages=(), stream=None, append=None):
         """Leaf of rank r grows by leaf_add[r] tokens (their K/V already in the
         pools), taking the pages it needs from new_pages in leaf-rank order;
-        the grouping is kept (tree_attn_plan_extend). Returns True when a
-        captured decode graph must be captured again."""
+        the grouping is kept (tree_attn_plan_extend). With append=(appender,
+        dst), appender from kv_appender, the new tokens' K/V are written in
+        the same call (tree_attn_plan_extend_append: one launch for both
+        device updates; the appender's stream is used when stream is None).
+        Returns True when a captured decode graph must be captured again."""
         n_leaves = self.n_queries // self.qpl
         add, add_a = _i32_addr(leaf_add)
         pages, pages_a = _i32_addr(new_pages)
         if len(add) != n_leaves:
             raise TreeAttnError(1, f"leaf_add must have one entry per leaf ({n_leaves})")
+        if stream is None and append is not None:
+            stream = append[0].stream
         if stream is None and not self.host_only:
             import torch
             stream = torch.cuda.current_stream().cuda_stream
         relaunch = ctypes.c_int32()
-        check(lib().tree_attn_plan_extend(self._handle, add_a, pages_a if len(pages) else None, len(pages),
-                                          stream or None, ctypes.byref(relaunch)))
+        if append is not None:
+            appender, dst = append
+            check(lib().tree_attn_plan_extend_append(self._handle, add_a, pages_a if len(pages) else None,
+                                                     len(pages), *appender.fused_args(dst), stream or None,
+                                                     ctypes.byref(relaunch)))
+        else:
+            check(lib().tree_attn_plan_extend(self._handle, add_a, pages_a if len(pages) else None, len(pages),
+                                              stream or None, ctypes.byref(relaunch)))
         if relaunch.value or self.host_only:
             self._info()
         return bool(relaunch.value)

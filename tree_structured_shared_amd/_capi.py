@@ -20,7 +20,7 @@ TABLE_COLS = {"groups": 8, "chunks": 3, "items": 5, "runs": 3}
 EXPORTED_SYMBOLS = [
     "tree_attn_plan", "tree_attn_decode", "tree_attn_plan_info", "tree_attn_plan_export",
     "tree_attn_timing_enable", "tree_attn_timing_read", "tree_attn_plan_destroy",
-    "tree_attn_last_error", "tree_attn_plan_extend", "tree_attn_kv_append",
+    "tree_attn_last_error", "tree_attn_plan_extend", "tree_attn_kv_append", "tree_attn_plan_extend_append",
 ]
 
 
@@ -78,6 +78,10 @@ def lib():
     L.tree_attn_kv_append.argtypes = [ctypes.POINTER(PagedKV), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     L.tree_attn_kv_append.restype = ctypes.c_int
+    L.tree_attn_plan_extend_append.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                               ctypes.POINTER(PagedKV), ctypes.c_void_p, ctypes.c_void_p,
+                                               ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, i32p]
+    L.tree_attn_plan_extend_append.restype = ctypes.c_int
     L.tree_attn_plan_info.argtypes = [ctypes.c_void_p, i32p, ctypes.POINTER(ctypes.c_int64), i32p]
     L.tree_attn_plan_info.restype = ctypes.c_int
     L.tree_attn_plan_export.argtypes = [ctypes.c_void_p, ctypes.c_int32, i32p,

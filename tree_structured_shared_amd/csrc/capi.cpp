@@ -269,7 +269,10 @@ ta_status upload(ta_plan* p) {
 // Decode-loop update of the device tables in place: the regions that changed
 // (and the page-table words of the grown segments) go through pinned staging
 // and one copy, then one kernel scatters them, all in order on `s`.
-ta_status upload_incremental(ta_plan* p, hipStream_t s) {
+// app (may be NULL): KV rows to append in the same launch as the table
+// update; *app_done says whether they were enqueued here.
+ta_status upload_incremental(ta_plan* p, hipStream_t s, const ta::AppendArgs* app, bool* app_done) {
+  *app_done = false;
   const ta::PlanTables& T = p->T;
   if (int64_t(T.n_slots) * p->n_qheads >= int64_t(INT32_MAX))
     return set_err(TA_EINVAL, "tree_attn_plan_extend: partial slots x q-heads exceed 32-bit workspace indices");
@@ -328,13 +331,104 @@ ta_status upload_incremental(ta_plan* p, hipStream_t s) {
     return hip_err(e, "tree_attn_plan_extend: hipEventCreate");
   std::memcpy(p->h_stage[b], desc.data(), desc.size() * 4);
   std::memcpy(p->h_stage[b] + desc.size(), data.data(), data.size() * 4);
-  if ((e = ta::launch_scatter(static_cast<int32_t*>(p->d_tables), int64_t(p->tables_words), p->h_stage[b],
-                              n_desc, s)) != hipSuccess)
-    return hip_err(e, "tree_attn_plan_extend: table update launch");
+  e = app ? ta::launch_append_scatter(*app, static_cast<int32_t*>(p->d_tables), int64_t(p->tables_words),
+                                      p->h_stage[b], n_desc, s)
+          : ta::launch_scatter(static_cast<int32_t*>(p->d_tables), int64_t(p->tables_words), p->h_stage[b], n_desc, s);
+  if (e != hipSuccess) return hip_err(e, "tree_attn_plan_extend: table update launch");
+  *app_done = app != nullptr;
   if ((e = hipEventRecord(p->stage_done[b], s)) != hipSuccess)
     return hip_err(e, "tree_attn_plan_extend: hipEventRecord");
   p->stage_used[b] = true;
   p->stage_next = b ^ 1;
+  return TA_OK;
+}
+
+// tree_attn_plan_extend, with app (may be NULL) appended on the same stream:
+// in the table update's launch when the tables are updated in place, else by
+// a launch of its own after them.
+ta_status extend_impl(ta_plan* plan, const int32_t* leaf_add, const int32_t* new_pages, int64_t n_new_pages,
+                      void* hip_stream, int32_t* relaunch, const ta::AppendArgs* app) {
+  try {
+    if (!plan->host_only) {
+      int dev = -1;
+      hipError_t e = hipGetDevice(&dev);
+      if (e != hipSuccess) return hip_err(e, "tree_attn_plan_extend: hipGetDevice");
+      if (dev != plan->device)
+        return set_err(TA_EINVAL, "tree_attn_plan_extend: current device differs from the plan's");
+    }
+    const int32_t old_items = plan->T.n_items, old_stream = plan->T.n_stream_items, old_slots = plan->T.n_slots;
+    std::string err;
+    const int rc = ta::plan_extend(plan->S, leaf_add, new_pages, n_new_pages, &err);
+    if (rc != 0) return set_err(ta_status(rc), err);
+    ta::plan_layout(plan->S, plan->T);
+    if (plan->host_only) return TA_OK;
+    size_t need[6];
+    region_sizes(plan, need);
+    bool fits = plan->sized_for_growth;
+    for (int x = 0; x < 6; ++x) fits = fits && need[x] <= plan->reg_cap[x];
+    fits = fits && workspace_need(plan) <= plan->ws_cap;
+    bool moved = false, app_done = false;
+    ta_status st;
+    if (fits) {
+      st = upload_incremental(plan, static_cast<hipStream_t>(hip_stream), app, &app_done);
+      set_workspace_ptrs(plan);
+      plan->ws_bytes = workspace_need(plan);
+    } else {
+      // first extend, or regions outgrown: wait for every enqueued use of the
+      // old tables, then upload them whole with room to grow (2x)
+      hipError_t e = hipDeviceSynchronize();
+      if (e != hipSuccess) return hip_err(e, "tree_attn_plan_extend: hipDeviceSynchronize");
+      st = upload_full(plan, true, &moved);
+      plan->sized_for_growth = true;
+    }
+    if (st != TA_OK) return st;
+    if (app && !app_done) {
+      const hipError_t e = ta::launch_append(*app, static_cast<hipStream_t>(hip_stream));
+      if (e != hipSuccess) return hip_err(e, "tree_attn_plan_extend_append: append launch");
+    }
+    if (relaunch)
+      *relaunch = (moved || plan->T.n_items != old_items || plan->T.n_stream_items != old_stream ||
+                   plan->T.n_slots != old_slots) ? 1 : 0;
+    return TA_OK;
+  } catch (const std::bad_alloc&) {
+    return set_err(TA_ENOMEM, "tree_attn_plan_extend: host allocation failed");
+  }
+}
+
+// Checks the arguments of a KV append (fn names the entry point in errors)
+// and fills *a; a->n_tokens == 0 means nothing to append.
+ta_status append_args(const char* fn, const ta_paged_kv* kv, const void* k_new, const void* v_new, int64_t n_tokens,
+                      int32_t n_kvheads, int32_t head_dim, const int32_t* dst, ta::AppendArgs* a) {
+  const std::string f(fn);
+  if (!kv || !kv->k || !kv->v) return set_err(TA_EINVAL, f + ": NULL pool");
+  if (n_tokens < 0) return set_err(TA_EINVAL, f + ": negative token count");
+  if (n_tokens > 0 && (!k_new || !v_new || !dst)) return set_err(TA_EINVAL, f + ": NULL argument");
+  if (kv->dtype != TA_F32 && kv->dtype != TA_BF16)
+    return set_err(TA_EUNSUPPORTED, f + ": dtype must be TA_F32 or TA_BF16");
+  if (head_dim != 64 && head_dim != 128) return set_err(TA_EUNSUPPORTED, f + ": head_dim must be 64 or 128");
+  if (n_kvheads < 1 || kv->page_size < 1 || kv->page_size > 256 || kv->n_pages < 1)
+    return set_err(TA_EINVAL, f + ": bad n_kvheads, page_size or n_pages");
+  const int64_t es = kv->dtype == TA_BF16 ? 2 : 4, vec = 16 / es;
+  if (kv->stride_page <= 0 || kv->stride_token <= 0 || kv->stride_head <= 0 ||
+      kv->stride_page % vec || kv->stride_token % vec || kv->stride_head % vec)
+    return set_err(TA_EINVAL, f + ": strides must be positive multiples of 16 bytes");
+  if ((reinterpret_cast<uintptr_t>(kv->k) | reinterpret_cast<uintptr_t>(kv->v) |
+       reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15)
+    return set_err(TA_EINVAL, f + ": pointers must be 16-byte aligned");
+  *a = ta::AppendArgs{};
+  a->k_new = static_cast<const char*>(k_new);
+  a->v_new = static_cast<const char*>(v_new);
+  a->k = static_cast<char*>(const_cast<void*>(kv->k));
+  a->v = static_cast<char*>(const_cast<void*>(kv->v));
+  a->dst = dst;
+  a->n_tokens = n_tokens;
+  a->n_pages = kv->n_pages;
+  a->sp_bytes = kv->stride_page * es;
+  a->st_bytes = kv->stride_token * es;
+  a->sh_bytes = kv->stride_head * es;
+  a->n_kvheads = n_kvheads;
+  a->row_bytes = int32_t(head_dim * es);
+  a->page_size = kv->page_size;
   return TA_OK;
 }
 
@@ -423,52 +517,30 @@ ta_status tree_attn_plan(const int32_t* parent, int32_t n_nodes, const int32_t* 
   }
 }
 
+
 ta_status tree_attn_plan_extend(ta_plan* plan, const int32_t* leaf_add, const int32_t* new_pages,
                                 int64_t n_new_pages, void* hip_stream, int32_t* relaunch) {
   g_err.clear();
   if (relaunch) *relaunch = 0;
   if (!plan) return set_err(TA_EINVAL, "tree_attn_plan_extend: plan is NULL");
-  try {
-    if (!plan->host_only) {
-      int dev = -1;
-      hipError_t e = hipGetDevice(&dev);
-      if (e != hipSuccess) return hip_err(e, "tree_attn_plan_extend: hipGetDevice");
-      if (dev != plan->device)
-        return set_err(TA_EINVAL, "tree_attn_plan_extend: current device differs from the plan's");
-    }
-    const int32_t old_items = plan->T.n_items, old_stream = plan->T.n_stream_items, old_slots = plan->T.n_slots;
-    std::string err;
-    const int rc = ta::plan_extend(plan->S, leaf_add, new_pages, n_new_pages, &err);
-    if (rc != 0) return set_err(ta_status(rc), err);
-    ta::plan_layout(plan->S, plan->T);
-    if (plan->host_only) return TA_OK;
-    size_t need[6];
-    region_sizes(plan, need);
-    bool fits = plan->sized_for_growth;
-    for (int x = 0; x < 6; ++x) fits = fits && need[x] <= plan->reg_cap[x];
-    fits = fits && workspace_need(plan) <= plan->ws_cap;
-    bool moved = false;
-    ta_status st;
-    if (fits) {
-      st = upload_incremental(plan, static_cast<hipStream_t>(hip_stream));
-      set_workspace_ptrs(plan);
-      plan->ws_bytes = workspace_need(plan);
-    } else {
-      // first extend, or regions outgrown: wait for every enqueued use of the
-      // old tables, then upload them whole with room to grow (2x)
-      hipError_t e = hipDeviceSynchronize();
-      if (e != hipSuccess) return hip_err(e, "tree_attn_plan_extend: hipDeviceSynchronize");
-      st = upload_full(plan, true, &moved);
-      plan->sized_for_growth = true;
-    }
-    if (st != TA_OK) return st;
-    if (relaunch)
-      *relaunch = (moved || plan->T.n_items != old_items || plan->T.n_stream_items != old_stream ||
-                   plan->T.n_slots != old_slots) ? 1 : 0;
-    return TA_OK;
-  } catch (const std::bad_alloc&) {
-    return set_err(TA_ENOMEM, "tree_attn_plan_extend: host allocation failed");
-  }
+  return extend_impl(plan, leaf_add, new_pages, n_new_pages, hip_stream, relaunch, nullptr);
+}
+
+ta_status tree_attn_plan_extend_append(ta_plan* plan, const int32_t* leaf_add, const int32_t* new_pages,
+                                       int64_t n_new_pages, const ta_paged_kv* kv, const void* k_new,
+                                       const void* v_new, int64_t n_tokens, const int32_t* dst, void* hip_stream,
+                                       int32_t* relaunch) {
+  g_err.clear();
+  if (relaunch) *relaunch = 0;
+  if (!plan) return set_err(TA_EINVAL, "tree_attn_plan_extend_append: plan is NULL");
+  if (plan->host_only) return set_err(TA_EINVAL, "tree_attn_plan_extend_append: plan was built host_only");
+  if (kv && kv->page_size != plan->page_size)
+    return set_err(TA_EINVAL, "tree_attn_plan_extend_append: pool page_size differs from the plan's");
+  ta::AppendArgs a;
+  const ta_status st = append_args("tree_attn_plan_extend_append", kv, k_new, v_new, n_tokens, plan->n_kvheads,
+                                   plan->head_dim, dst, &a);
+  if (st != TA_OK) return st;
+  return extend_impl(plan, leaf_add, new_pages, n_new_pages, hip_stream, relaunch, n_tokens > 0 ? &a : nullptr);
 }
 
 ta_status tree_attn_decode(const void* q, ta_dtype q_dtype, const ta_paged_kv* kv,
@@ -562,36 +634,9 @@ ta_status tree_attn_decode(const void* q, ta_dtype q_dtype, const ta_paged_kv* k
 ta_status tree_attn_kv_append(const ta_paged_kv* kv, const void* k_new, const void* v_new, int64_t n_tokens,
                               int32_t n_kvheads, int32_t head_dim, const int32_t* dst, void* hip_stream) {
   g_err.clear();
-  if (!kv || !kv->k || !kv->v) return set_err(TA_EINVAL, "tree_attn_kv_append: NULL pool");
-  if (n_tokens < 0) return set_err(TA_EINVAL, "tree_attn_kv_append: negative token count");
-  if (n_tokens > 0 && (!k_new || !v_new || !dst)) return set_err(TA_EINVAL, "tree_attn_kv_append: NULL argument");
-  if (kv->dtype != TA_F32 && kv->dtype != TA_BF16)
-    return set_err(TA_EUNSUPPORTED, "tree_attn_kv_append: dtype must be TA_F32 or TA_BF16");
-  if (head_dim != 64 && head_dim != 128) return set_err(TA_EUNSUPPORTED, "tree_attn_kv_append: head_dim must be 64 or 128");
-  if (n_kvheads < 1 || kv->page_size < 1 || kv->page_size > 256 || kv->n_pages < 1)
-    return set_err(TA_EINVAL, "tree_attn_kv_append: bad n_kvheads, page_size or n_pages");
-  const int64_t es = kv->dtype == TA_BF16 ? 2 : 4, vec = 16 / es;
-  if (kv->stride_page <= 0 || kv->stride_token <= 0 || kv->stride_head <= 0 ||
-      kv->stride_page % vec || kv->stride_token % vec || kv->stride_head % vec)
-    return set_err(TA_EINVAL, "tree_attn_kv_append: strides must be positive multiples of 16 bytes");
-  if ((reinterpret_cast<uintptr_t>(kv->k) | reinterpret_cast<uintptr_t>(kv->v) |
-       reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15)
-    return set_err(TA_EINVAL, "tree_attn_kv_append: pointers must be 16-byte aligned");
-  if (n_tokens == 0) return TA_OK;
-  ta::AppendArgs a{};
-  a.k_new = static_cast<const char*>(k_new);
-  a.v_new = static_cast<const char*>(v_new);
-  a.k = static_cast<char*>(const_cast<void*>(kv->k));
-  a.v = static_cast<char*>(const_cast<void*>(kv->v));
-  a.dst = dst;
-  a.n_tokens = n_tokens;
-  a.n_pages = kv->n_pages;
-  a.sp_bytes = kv->stride_page * es;
-  a.st_bytes = kv->stride_token * es;
-  a.sh_bytes = kv->stride_head * es;
-  a.n_kvheads = n_kvheads;
-  a.row_bytes = int32_t(head_dim * es);
-  a.page_size = kv->page_size;
+  ta::AppendArgs a;
+  const ta_status st = append_args("tree_attn_kv_append", kv, k_new, v_new, n_tokens, n_kvheads, head_dim, dst, &a);
+  if (st != TA_OK || n_tokens == 0) return st;
   const hipError_t e = ta::launch_append(a, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return hip_err(e, "tree_attn_kv_append: launch");
   return TA_OK;

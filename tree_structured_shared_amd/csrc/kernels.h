@@ -102,5 +102,9 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 // (it must stay unchanged until the kernel has run). The host checks every
 // range lies inside dst.
 hipError_t launch_scatter(int32_t* dst, int64_t dst_words, const int32_t* stage, int32_t n_desc, hipStream_t s);
+// launch_append and launch_scatter as one launch (their block ranges side by
+// side in one grid); either part may be empty.
+hipError_t launch_append_scatter(const AppendArgs& a, int32_t* dst, int64_t dst_words, const int32_t* stage,
+                                 int32_t n_desc, hipStream_t s);
 
 }  // namespace ta

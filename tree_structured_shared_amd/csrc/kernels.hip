@@ -1184,21 +1184,25 @@ __global__ __launch_bounds__(kBlock) void lse_reduce_kernel(ReduceArgs a) {
 
 // One workgroup per descriptor (grid-stride over descriptors); the stage is
 // pinned host memory, read over the bus.
-__global__ void scatter_kernel(int32_t* dst, int64_t dst_words, const int32_t* stage, int32_t n_desc) {
-  for (int32_t d = blockIdx.x; d < n_desc; d += gridDim.x) {
+// Table update by blocks [0, nb) of a launch (block b takes descriptors b,
+// b + nb, ...).
+__device__ __forceinline__ void scatter_blocks(int32_t* dst, int64_t dst_words, const int32_t* stage,
+                                               int32_t n_desc, int32_t b, int32_t nb) {
+  for (int32_t d = b; d < n_desc; d += nb) {
     const int64_t to = stage[3 * d], n = stage[3 * d + 1], from = stage[3 * d + 2];
     for (int64_t x = threadIdx.x; x < n; x += blockDim.x)
       if (to + x < dst_words) dst[to + x] = stage[from + x];
   }
 }
 
-// KV append: 16 lanes per 256-byte head row (16 bytes each), grid-stride over
-// (token, kv-head) rows; a destination outside the pool is skipped.
-__global__ void append_kernel(AppendArgs a) {
+// KV append by blocks [0, nb) of a launch: 16 lanes per 256-byte head row (16
+// bytes each), block-stride over (token, kv-head) rows; a destination outside
+// the pool is skipped.
+__device__ __forceinline__ void append_blocks(const AppendArgs& a, int64_t b, int64_t nb) {
   const int64_t rows = a.n_tokens * a.n_kvheads;
   const int chunks = a.row_bytes >> 4;  // 16-byte pieces per head row
-  const int64_t step = int64_t(gridDim.x) * blockDim.x;
-  for (int64_t x = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; x < rows * chunks; x += step) {
+  const int64_t step = nb * blockDim.x;
+  for (int64_t x = b * blockDim.x + threadIdx.x; x < rows * chunks; x += step) {
     const int64_t row = x / chunks;
     const int c = int(x - row * chunks);
     const int64_t r = row / a.n_kvheads;
@@ -1212,6 +1216,23 @@ __global__ void append_kernel(AppendArgs a) {
     *reinterpret_cast<u32x4*>(a.k + off) = *reinterpret_cast<const u32x4*>(a.k_new + src);
     *reinterpret_cast<u32x4*>(a.v + off) = *reinterpret_cast<const u32x4*>(a.v_new + src);
   }
+}
+
+__global__ void scatter_kernel(int32_t* dst, int64_t dst_words, const int32_t* stage, int32_t n_desc) {
+  scatter_blocks(dst, dst_words, stage, n_desc, int32_t(blockIdx.x), int32_t(gridDim.x));
+}
+
+__global__ void append_kernel(AppendArgs a) { append_blocks(a, blockIdx.x, gridDim.x); }
+
+// Both updates of a decode-loop step in one launch: the first sb blocks
+// update the tables, the rest append the new K/V rows (the two touch
+// disjoint memory).
+__global__ void update_kernel(AppendArgs a, int32_t* dst, int64_t dst_words, const int32_t* stage, int32_t n_desc,
+                              int32_t sb) {
+  if (int32_t(blockIdx.x) < sb)
+    scatter_blocks(dst, dst_words, stage, n_desc, int32_t(blockIdx.x), sb);
+  else
+    append_blocks(a, int64_t(blockIdx.x) - sb, int64_t(gridDim.x) - sb);
 }
 
 __global__ void fill_kernel(float* p, int64_t n, float value) {
@@ -1287,11 +1308,25 @@ hipError_t launch_scatter(int32_t* dst, int64_t dst_words, const int32_t* stage,
   return hipGetLastError();
 }
 
-hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
+static int64_t append_grid(const AppendArgs& a) {
   const int64_t work = a.n_tokens * a.n_kvheads * (a.row_bytes >> 4);
-  if (work <= 0) return hipSuccess;
-  const int64_t blocks = std::min<int64_t>((work + 255) / 256, 8192);
+  return work <= 0 ? 0 : std::min<int64_t>((work + 255) / 256, 8192);
+}
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
+  const int64_t blocks = append_grid(a);
+  if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(append_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_scatter(const AppendArgs& a, int32_t* dst, int64_t dst_words, const int32_t* stage,
+                                 int32_t n_desc, hipStream_t s) {
+  const int64_t ab = append_grid(a);
+  if (ab == 0) return launch_scatter(dst, dst_words, stage, n_desc, s);
+  if (n_desc <= 0) return launch_append(a, s);
+  const int32_t sb = std::min(n_desc, 1024);
+  hipLaunchKernelGGL(update_kernel, dim3(unsigned(sb + ab)), dim3(256), 0, s, a, dst, dst_words, stage, n_desc, sb);
   return hipGetLastError();
 }
 
