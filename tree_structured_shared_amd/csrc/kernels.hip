@@ -130,10 +130,12 @@ __device__ __forceinline__ float xor32(float v) {
 }
 // max / sum over lanes l, l^16, l^32, l^48
 __device__ __forceinline__ float max4rows(float v) {
+  // each swap returns the lane's own value and its partner's; v (already
+  // quiet) leads a three-input max, which takes the swapped values as they are
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  v = fmaxf(fmaxf(v, __uint_as_float(a[0])), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return fmaxf(fmaxf(v, __uint_as_float(b[0])), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float sum4rows(float v) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -530,7 +532,13 @@ __device__ __forceinline__ void mfma_softmax(MfmaState<D, NRTW>& S, int k, const
       if (16 + 4 * j + x >= lim) sv[4 + x] = TA_NEG_INF;
     }
   }
-  float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+  // four three-input maxes (sv[0] enters twice to make nine operands):
+  // v_max3_f32 takes the matrix-core results as they are, where a tree of
+  // two-input maxes first quiets each operand with an instruction of its own
+  float mx = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
+  mx = fmaxf(fmaxf(mx, sv[3]), sv[4]);
+  mx = fmaxf(fmaxf(mx, sv[5]), sv[6]);
+  mx = fmaxf(fmaxf(mx, sv[7]), sv[0]);
   mx = max4rows(mx) * c;  // c > 0: the max of scaled scores
   const bool raise = mx > S.m[k] + kRescale;
   if (__builtin_amdgcn_ballot_w64(raise)) {  // rare after the first tiles
