@@ -217,7 +217,8 @@ def test_decode_loop_append_extend_decode():
     plan.close()
 
 
-def test_fused_append_extend_matches_separate_calls():
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.float32, 64)])
+def test_fused_append_extend_matches_separate_calls(dtype, d):
     """tree_attn_plan_extend_append (one launch for the KV append and the
     table update) against tree_attn_kv_append + tree_attn_plan_extend on a
     twin plan and twin pools: the same pools, tables and (bit-identical)
@@ -225,7 +226,12 @@ def test_fused_append_extend_matches_separate_calls():
     first extend (tables uploaded whole), in-place updates, a step that
     outgrows a leaf's page-table slack and a step with no new tokens."""
     from tree_structured_shared_amd import kv_append, kv_appender
-    inst = _small_tree(torch.bfloat16, 2)
+    if d == 128:
+        inst = _small_tree(dtype, 2)
+    else:
+        inst = synth.make_tree([-1, 0, 0, 1, 1, 2, 0], [300, 40, 70, 20, 33, 16, 7], page_size=16, qpl=2,
+                               n_qheads=16, n_kvheads=4, head_dim=d, dtype=dtype, seed=2)
+        inst = synth.fill_tensors(inst, seed=42)
     spare = 96
     pools = []
     for _ in range(2):
