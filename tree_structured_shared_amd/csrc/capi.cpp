@@ -310,6 +310,17 @@ ta_status upload_incremental(ta_plan* p, hipStream_t s, const ta::AppendArgs* ap
   const size_t words = desc.size() + data.size();
   if (words >= size_t(INT32_MAX)) return set_err(TA_EINVAL, "tree_attn_plan_extend: update too large");
   hipError_t e;
+  if (words <= size_t(ta::kArgStageWords)) {
+    // small update: descriptors and words travel in the kernel arguments
+    ta::ArgStage st;
+    std::memcpy(st.w, desc.data(), desc.size() * 4);
+    std::memcpy(st.w + desc.size(), data.data(), data.size() * 4);
+    if ((e = ta::launch_update_args(app, static_cast<int32_t*>(p->d_tables), int64_t(p->tables_words), st, n_desc,
+                                    s)) != hipSuccess)
+      return hip_err(e, "tree_attn_plan_extend: table update launch");
+    *app_done = app != nullptr;
+    return TA_OK;
+  }
   // pinned host staging, read by the scatter kernel in place: this buffer's
   // previous scatter must have run
   const int b = p->stage_next;

@@ -106,5 +106,15 @@ hipError_t launch_scatter(int32_t* dst, int64_t dst_words, const int32_t* stage,
 // side in one grid); either part may be empty.
 hipError_t launch_append_scatter(const AppendArgs& a, int32_t* dst, int64_t dst_words, const int32_t* stage,
                                  int32_t n_desc, hipStream_t s);
+// A table update small enough to travel in the kernel arguments (descriptors
+// and words as in launch_scatter, at most kArgStageWords words in all): the
+// kernel reads them from its argument segment, with no read of host memory.
+// app (may be NULL) is appended in the same launch.
+constexpr int kArgStageWords = 448;
+struct ArgStage {
+  int32_t w[kArgStageWords];
+};
+hipError_t launch_update_args(const AppendArgs* app, int32_t* dst, int64_t dst_words, const ArgStage& stage,
+                              int32_t n_desc, hipStream_t s);
 
 }  // namespace ta

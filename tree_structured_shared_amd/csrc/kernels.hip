@@ -1243,6 +1243,16 @@ __global__ void update_kernel(AppendArgs a, int32_t* dst, int64_t dst_words, con
     append_blocks(a, int64_t(blockIdx.x) - sb, int64_t(gridDim.x) - sb);
 }
 
+// The same with the staged words in the kernel arguments (read in place from
+// the argument segment).
+__global__ void update_args_kernel(AppendArgs a, int32_t* dst, int64_t dst_words, ArgStage st, int32_t n_desc,
+                                   int32_t sb) {
+  if (int32_t(blockIdx.x) < sb)
+    scatter_blocks(dst, dst_words, st.w, n_desc, int32_t(blockIdx.x), sb);
+  else
+    append_blocks(a, int64_t(blockIdx.x) - sb, int64_t(gridDim.x) - sb);
+}
+
 __global__ void fill_kernel(float* p, int64_t n, float value) {
   for (int64_t x = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; x < n; x += int64_t(gridDim.x) * blockDim.x)
     p[x] = value;
@@ -1325,6 +1335,18 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
   const int64_t blocks = append_grid(a);
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(append_kernel, dim3(unsigned(blocks)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_update_args(const AppendArgs* app, int32_t* dst, int64_t dst_words, const ArgStage& stage,
+                              int32_t n_desc, hipStream_t s) {
+  AppendArgs a{};
+  if (app) a = *app;  // else n_tokens = 0: no append blocks
+  const int64_t ab = append_grid(a);
+  const int32_t sb = std::max(0, std::min(n_desc, 64));
+  if (sb + ab == 0) return hipSuccess;
+  hipLaunchKernelGGL(update_args_kernel, dim3(unsigned(sb + ab)), dim3(256), 0, s, a, dst, dst_words, stage,
+                     n_desc, sb);
   return hipGetLastError();
 }
 
