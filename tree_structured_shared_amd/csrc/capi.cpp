@@ -312,7 +312,7 @@ ta_status upload_incremental(ta_plan* p, hipStream_t s, const ta::AppendArgs* ap
   hipError_t e;
   if (words <= size_t(ta::kArgStageWords)) {
     // small update: descriptors and words travel in the kernel arguments
-    ta::ArgStage st;
+    ta::ArgStage st{};
     std::memcpy(st.w, desc.data(), desc.size() * 4);
     std::memcpy(st.w + desc.size(), data.data(), data.size() * 4);
     if ((e = ta::launch_update_args(app, static_cast<int32_t*>(p->d_tables), int64_t(p->tables_words), st, n_desc,

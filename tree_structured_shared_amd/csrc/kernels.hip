@@ -1244,7 +1244,10 @@ __global__ void update_kernel(AppendArgs a, int32_t* dst, int64_t dst_words, con
 }
 
 // The same with the staged words in the kernel arguments (read in place from
-// the argument segment).
+// the argument segment). The whole argument list stays within 4 KiB.
+static_assert(sizeof(AppendArgs) + sizeof(int32_t*) + sizeof(int64_t) + sizeof(ArgStage) + 2 * sizeof(int32_t) +
+                      64 <= 4096,
+              "update_args_kernel's arguments fit a 4 KiB argument block");
 __global__ void update_args_kernel(AppendArgs a, int32_t* dst, int64_t dst_words, ArgStage st, int32_t n_desc,
                                    int32_t sb) {
   if (int32_t(blockIdx.x) < sb)
