@@ -258,11 +258,24 @@ def build_plan(parent, node_len, node_page_ptr, node_page_ids, page_size, qpl,
         single = G["rows"] <= o["stream_rows"] and not (o["tile_join"] and has_wg and G["rows"] >= TILE_ROWS)
         G["cls"] = 0 if single else 1
         if G["cls"] == 0:
-            G["nblocks"], G["rb"] = 1, G["rows"]
-        else:   # balanced blocks of at most rb rows, 16-aligned when rb is
+            G["blocks"] = [(0, G["rows"])]
+        else:
+            # as few blocks of at most rb rows as possible, even in whole
+            # tiles: the tiles of the group are dealt out so that the first
+            # (tiles mod blocks) blocks hold one more; the last block ends
+            # at the group's last row
+            tile = TILE_ROWS if rb % TILE_ROWS == 0 else 1
             nb = _cdiv(G["rows"], rb)
-            G["rb"] = _align_up(_cdiv(G["rows"], nb), 16 if rb % 16 == 0 else 1)
-            G["nblocks"] = _cdiv(G["rows"], G["rb"])
+            n_tiles = _cdiv(G["rows"], tile)
+            G["blocks"] = []
+            t0 = 0
+            for b in range(nb):
+                nt = n_tiles // nb + (1 if b < n_tiles % nb else 0)
+                r0 = t0 * tile
+                G["blocks"].append((r0, min(G["rows"], r0 + nt * tile) - r0))
+                t0 += nt
+        G["nblocks"] = len(G["blocks"])
+        G["rb"] = max(nr for _, nr in G["blocks"])
     if o["split"]:
         W = H * sum((3 if G["cls"] == 0 else BLOCK_WAVE_WEIGHT3) * G["nblocks"] * G["kv_len"]
                     for G in groups)
@@ -289,9 +302,7 @@ def build_plan(parent, node_len, node_page_ptr, node_page_ids, page_size, qpl,
     # class longest first (stable on (group, block, chunk))
     items = []
     for gi, G in enumerate(groups):
-        for b in range(G["nblocks"]):
-            r0 = b * G["rb"]
-            nr = min(G["rows"], r0 + G["rb"]) - r0
+        for r0, nr in G["blocks"]:
             for c in range(G["n_chunks"]):
                 ci = G["chunk_ptr"] + c
                 est = (chunks[ci][2] - chunks[ci][1]) * (ITEM_FIXED_COST + nr)

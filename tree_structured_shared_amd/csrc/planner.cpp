@@ -261,10 +261,10 @@ int plan_init(const int32_t* parent, int32_t n, const int32_t* node_len,
     if (G.cls == 0) {
       G.nblocks = 1;
       G.rb = G.rows;
-    } else {  // balanced blocks of at most rb rows, 16-aligned when rb is
-      const int64_t nb = cdiv(G.rows, p.rb);
-      G.rb = int32_t(align_up(cdiv(G.rows, nb), p.rb % 16 == 0 ? 16 : 1));
-      G.nblocks = int32_t(cdiv(G.rows, G.rb));
+    } else {  // as few blocks of at most rb rows as possible, even in whole tiles
+      G.tile = p.rb % kTileRows == 0 ? kTileRows : 1;
+      G.nblocks = int32_t(cdiv(G.rows, p.rb));
+      G.rb = int32_t(std::min<int64_t>(G.rows, cdiv(cdiv(G.rows, G.tile), G.nblocks) * G.tile));
     }
   }
 
@@ -287,6 +287,22 @@ int plan_init(const int32_t* parent, int32_t n, const int32_t* node_len,
   }
   *out = std::move(S);
   return 0;
+}
+
+// Row block b of a group: a workgroup group's rows in whole tiles of G.tile
+// rows, spread over its blocks as evenly as the tiles allow (the first
+// tiles % nblocks blocks take one tile more); the last block ends at the
+// group's last row.
+static void row_block(const PlanGroup& G, int32_t b, int32_t* r0, int32_t* nr) {
+  if (G.cls == 0) {
+    *r0 = 0;
+    *nr = G.rows;
+    return;
+  }
+  const int32_t T = int32_t(cdiv(G.rows, G.tile)), base = T / G.nblocks, extra = T % G.nblocks;
+  const int32_t t0 = b * base + std::min(b, extra), nt = base + (b < extra ? 1 : 0);
+  *r0 = t0 * G.tile;
+  *nr = std::min(G.rows, *r0 + nt * G.tile) - *r0;
 }
 
 void plan_layout(PlanState& S, PlanTables& T) {
@@ -340,8 +356,8 @@ void plan_layout(PlanState& S, PlanTables& T) {
   for (int32_t gi = 0; gi < int32_t(S.groups.size()); ++gi) {
     const PlanGroup& G = S.groups[gi];
     for (int32_t b = 0; b < G.nblocks; ++b) {
-      const int32_t r0 = b * G.rb;
-      const int32_t nr = std::min(G.rows, r0 + G.rb) - r0;
+      int32_t r0, nr;
+      row_block(G, b, &r0, &nr);
       for (int32_t c = 0; c < G.n_chunks; ++c) {
         const int32_t ci = G.chunk_ptr + c;
         items.push_back({int64_t(T.chunks[3 * ci + 2] - T.chunks[3 * ci + 1]) * (kItemFixedCost + nr), gi, r0, nr,

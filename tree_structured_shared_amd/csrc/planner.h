@@ -57,6 +57,7 @@ struct PlanTables {
 // the node lengths.
 struct PlanGroup {
   int32_t node = 0, top = 0, rows = 0, nblocks = 0, rb = 0, cls = 0;
+  int32_t tile = 1;  // row blocks are made of whole tiles of this many rows
   bool grows = false;  // the segment ends at a leaf: the group grows in a decode loop
   std::vector<int32_t> qs, seg;
   int32_t kv_len = 0, chunk_ptr = 0, n_chunks = 0, slot_base = 0, q_ptr = 0;
