@@ -76,6 +76,12 @@ typedef struct {
   int32_t no_tile_join;      /* 1 = groups of 16 or more rows stay single-wave items (when
                                 at most stream_rows) even if the plan has workgroup items;
                                 default 0: they join the workgroup items */
+  int32_t fail_alloc_after;  /* testing: the plan's N-th allocation step fails with
+                                TA_ENOMEM as if memory ran out (0 = never). Steps, in order:
+                                1 the plan object, 2 the planner state, 3 its tables, then
+                                (device plans) 4 the device tables, 5 the workspace; each
+                                tree_attn_plan_extend adds one host step first, then its
+                                device steps (staging, regrown tables and workspace) */
 } ta_plan_opts;
 
 /* Paged K/V pools on the device. Element strides; head_dim is contiguous.
@@ -117,7 +123,8 @@ ta_status tree_attn_plan(const int32_t* parent, int32_t n_nodes, const int32_t* 
  *  out : device [n_queries, n_qheads, head_dim] fp32, contiguous.
  * Asynchronous: returns after enqueueing. One plan serves one decode in
  * flight at a time (its workspace is shared); the plan must outlive the work.
- * TA_EINVAL for null pointers, dtype/page mismatches or page ids >= n_pages. */
+ * TA_EINVAL for null pointers, dtype/page mismatches or page ids >= n_pages,
+ * and for a plan left unusable by a failed tree_attn_plan_extend. */
 ta_status tree_attn_decode(const void* q, ta_dtype q_dtype, const ta_paged_kv* kv,
                            const ta_plan* plan, float* out, void* hip_stream);
 
@@ -143,8 +150,10 @@ ta_status tree_attn_decode(const void* q, ta_dtype q_dtype, const ta_paged_kv* k
  * device address changed: a decode captured in a HIP graph must then be
  * captured again; with 0 the captured graph stays valid. Do not call while a
  * graph capture is in progress on hip_stream. host_only plans update their
- * tables only. All-or-nothing on TA_EINVAL (counts, page ids); a failed device
- * update (TA_EHIP, TA_ENOMEM) leaves the plan unusable for decode. */
+ * tables only. All-or-nothing on TA_EINVAL (counts, page ids); a failed
+ * update after the plan's tables have moved on (TA_EHIP, TA_ENOMEM) leaves
+ * the plan unusable: later extends and decodes return TA_EINVAL, and
+ * tree_attn_plan_destroy still frees it. */
 ta_status tree_attn_plan_extend(ta_plan* plan, const int32_t* leaf_add, const int32_t* new_pages,
                                 int64_t n_new_pages, void* hip_stream, int32_t* relaunch);
 

@@ -287,3 +287,100 @@ def random_small_tree(seed: int, *, max_nodes=24, max_len=80, page_size=None, qp
     if tensors:
         fill_tensors(inst, seed + 77)
     return inst
+
+
+# ---------------------------------------------------------------------------
+# Peaky logits. Real attention is rarely the flat softmax that N(0,1) inputs
+# give (score std ~1): heads put most of their mass on a few tokens (a sink on
+# the first token, a couple of dominant keys) and scores can rise along a
+# path. These helpers reshape an instance whose tensors are already drawn, so
+# that a test can make the softmax peaky on purpose. They only move Q/K/V
+# values; no attention arithmetic happens here.
+
+PEAK_KINDS = ("scaled_q", "ramp", "late_spike", "sink", "two_peaks", "two_peaks_antipodal")
+
+
+def _token_slots(inst, u):
+    """(page, slot) of every token of node u, in order."""
+    ps = inst.page_size
+    pages = inst.node_page_ids[inst.node_page_ptr[u]:inst.node_page_ptr[u + 1]]
+    return [(int(pages[t // ps]), t % ps) for t in range(int(inst.node_len[u]))]
+
+
+def plant_peaks(inst: TreeInstance, kind: str, seed: int, strength: float = 10.0) -> TreeInstance:
+    """Plant logit structure into inst's Q/K/V (in place; returns inst).
+
+    Every q-head of kv-head h gets a component sqrt(d) * u_h along a unit
+    vector u_h drawn per kv-head, so a key with a component b * u_h scores
+    about b higher (in natural-log units, after the 1/sqrt(d) scale) than
+    an unplanted one for every query of that kv-head. ``strength`` is that b
+    for the planted keys. Kinds:
+
+    * ``scaled_q``: Q multiplied by strength / 2.5 (score std ~4 at the
+      default strength), so many keys dominate and the running max rises
+      from tile to tile.
+    * ``ramp``: key t of the root gets (strength * 3 t / len) u_h (the
+      score rises ~3 strength along the root) and key t of every other node
+      strength * (0.5 + t / len) u_h: the running max is raised again and
+      again mid-chunk.
+    * ``late_spike``: three keys in the second half of the root and one in
+      the second half of each leaf get strength * u_h.
+    * ``sink``: the root's first key gets strength * u_h (an attention sink:
+      most of every query's mass on one token).
+    * ``two_peaks``: two root keys (positions len/3 and 5 len/6) get
+      strength * u_h and (strength - 0.3) * u_h: two near-equal dominant
+      keys with their own N(0,1) values.
+    * ``two_peaks_antipodal``: as two_peaks, with the second key's value set
+      to minus the first's (the largest value difference two N(0,1) rows
+      give, the worst case for rounding the two weights apart).
+    """
+    if kind not in PEAK_KINDS:
+        raise ValueError(f"unknown peak kind {kind}")
+    rng = np.random.default_rng(seed)
+    H, d = inst.n_kvheads, inst.head_dim
+    g = inst.n_qheads // H
+    u = rng.standard_normal((H, d))
+    u /= np.linalg.norm(u, axis=1, keepdims=True)
+    u = torch.from_numpy(u).to(torch.float32)
+    q = inst.q.to(torch.float32)
+    k = inst.k_pool.to(torch.float32)
+    v = inst.v_pool.to(torch.float32)
+    if kind == "scaled_q":
+        q = q * (strength / 2.5)
+    else:
+        q = q + math.sqrt(d) * u.repeat_interleave(g, dim=0)[None]
+        root = int(np.flatnonzero(inst.parent < 0)[0])
+        has_child = np.zeros(inst.n_nodes, bool)
+        has_child[inst.parent[inst.parent >= 0]] = True
+
+        def plant(node, t, b):
+            pg, sl = _token_slots(inst, node)[t]
+            k[pg, sl] += b * u
+
+        L = int(inst.node_len[root])
+        if kind == "ramp":
+            for node in range(inst.n_nodes):
+                n = int(inst.node_len[node])
+                for t in range(n):
+                    plant(node, t, strength * 3.0 * t / n if node == root else strength * (0.5 + t / n))
+        elif kind == "late_spike":
+            for t in (L // 2 + L // 7, (3 * L) // 4, L - 2):
+                plant(root, max(0, t), strength)
+            for node in np.flatnonzero(~has_child):
+                n = int(inst.node_len[node])
+                if node != root:
+                    plant(int(node), n // 2 + int(rng.integers(0, max(1, n - n // 2 - 1))), strength)
+        elif kind == "sink":
+            plant(root, 0, strength)
+        else:
+            a, b = L // 3, (5 * L) // 6
+            plant(root, a, strength)
+            plant(root, b, strength - 0.3)
+            if kind == "two_peaks_antipodal":
+                pa, sa = _token_slots(inst, root)[a]
+                pb, sb = _token_slots(inst, root)[b]
+                v[pb, sb] = -v[pa, sa]
+    inst.q = q.to(inst.dtype).contiguous()
+    inst.k_pool = k.to(inst.dtype).contiguous()
+    inst.v_pool = v.to(inst.dtype).contiguous()
+    return inst

@@ -4,31 +4,20 @@ their allocation) the decode of the grown tree matches the fp64 oracle, and
 a decode captured in a HIP graph replays the grown tree while extend reports
 no relaunch. Extends and decodes are enqueued back to back on one stream,
 without host synchronisation between them."""
-import sys
-
 import numpy as np
 import pytest
 import torch
 
 import synth
 from oracle import tree_attention as ta
+from parity_util import check as _check_np, log as _log
 from tree_structured_shared_amd import Plan
 
 pytestmark = pytest.mark.gpu
-TOL = 3e-3
-
-
-def _log(msg):
-    print(msg, flush=True)
-    sys.stdout.flush()
 
 
 def _check(got, ref, what):
-    got = got.cpu().numpy().astype(np.float64)
-    assert np.isfinite(got).all(), f"{what}: non-finite output"
-    err = np.nanmax(np.abs(got - ref))
-    _log(f"{what}: max-abs err {err:.3e}")
-    assert err <= TOL, f"{what}: max-abs err {err:.3e}"
+    _check_np(got.cpu().numpy().astype(np.float64), ref, what)
 
 
 def _small_tree(dtype, qpl):

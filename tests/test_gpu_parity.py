@@ -6,46 +6,16 @@ poisoned with NaN before each decode, so a partial the kernels fail to write
 shows up as NaN in the output; unused KV slots hold V = 1e30 canaries, so an
 unmasked stray read shows up as a huge value.
 """
-import sys
-
 import numpy as np
 import pytest
 import torch
 
 import synth
 from oracle import tree_attention as ta
+from parity_util import check as _check, dev as _dev, log as _log, run as _run
 from tree_structured_shared_amd import Plan, TreeAttnError
 
 pytestmark = pytest.mark.gpu
-TOL = 3e-3
-
-
-def _dev(inst):
-    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
-    return inst.q.cuda(), inst.k_pool.cuda(), inst.v_pool.cuda()
-
-
-def _run(inst, dev=None, **plan_kw):
-    q, k, v = dev if dev is not None else _dev(inst)
-    plan_kw.setdefault("poison_workspace", True)
-    plan = Plan.for_instance(inst, **plan_kw)
-    out = plan.decode(q, k, v)
-    torch.cuda.synchronize()
-    res = out.cpu().numpy().astype(np.float64)
-    plan.close()
-    return res
-
-
-def _log(msg):
-    print(msg, flush=True)
-    sys.stdout.flush()
-
-
-def _check(got, ref, what):
-    assert np.isfinite(got).all(), f"{what}: non-finite output"
-    err = np.nanmax(np.abs(got - ref))
-    _log(f"{what}: max-abs err {err:.3e}")
-    assert err <= TOL, f"{what}: max-abs err {err:.3e}"
 
 
 @pytest.mark.parametrize("k", [1, 2, 3, 4])

@@ -4,7 +4,10 @@ from __future__ import annotations
 import ctypes
 import os
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtree_attn.so")
+# TREE_ATTN_LIB names another build of the same library (the host-sanitized
+# build of the CPU tests); by default the in-tree libtree_attn.so.
+_LIB_PATH = os.environ.get("TREE_ATTN_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                             "libtree_attn.so")
 
 TA_OK, TA_EINVAL, TA_ENOMEM, TA_EHIP, TA_EUNSUPPORTED = range(5)
 TA_F32, TA_BF16 = 0, 1
@@ -33,6 +36,7 @@ class PlanOpts(ctypes.Structure):
         ("scale", ctypes.c_float), ("poison_workspace", ctypes.c_int32),
         ("stream_rows", ctypes.c_int32),
         ("split_align", ctypes.c_int32), ("no_tile_join", ctypes.c_int32),
+        ("fail_alloc_after", ctypes.c_int32),
     ]
 
 

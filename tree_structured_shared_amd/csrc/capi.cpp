@@ -7,6 +7,8 @@
 #include <algorithm>
 #include <climits>
 #include <cmath>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -69,6 +71,12 @@ struct ta_plan {
   // 4 per timed decode: start/stop of the partial kernel and of the reduction
   std::vector<hipEvent_t> ev;
   int32_t timing_cap = 0, timing_n = 0;
+  // false after a device update failed part-way (the device tables or the
+  // workspace may be gone): decode refuses the plan from then on
+  bool usable = true;
+  // testing (ta_plan_opts.fail_alloc_after): the plan's fail_after-th
+  // allocation step fails as if out of memory; alloc_steps counts the steps
+  int32_t fail_after = 0, alloc_steps = 0;
 };
 
 namespace {
@@ -100,6 +108,11 @@ const std::vector<int32_t>* table_ptr(const ta_plan* p, int32_t id) {
   }
 }
 
+// One allocation step of a plan (plan object, planner state, tables, device
+// tables, workspace, staging): true when the testing option asks this step
+// to fail.
+bool alloc_fails(ta_plan* p) { return p->fail_after > 0 && ++p->alloc_steps == p->fail_after; }
+
 void free_device(ta_plan* p) {
   if (p->host_only) return;
   for (hipEvent_t e : p->ev) (void)hipEventDestroy(e);
@@ -124,12 +137,6 @@ constexpr int kWordsPerItem = int(sizeof(ta::WorkItem) / 4);
 // partials are contiguous in path order and the reduction needs no slot list).
 void device_forms(ta_plan* p) {
   const ta::PlanTables& T = p->T;
-  // visible tokens of each query over its whole path (sum over its groups)
-  std::vector<int64_t> q_vis(T.n_queries, 0);
-  for (int32_t gi = 0; gi < T.n_groups; ++gi) {
-    const int32_t* G = &T.groups[8 * gi];
-    for (int32_t x = 0; x < G[3]; ++x) q_vis[T.group_qs[G[4] + x]] += T.group_vis[G[4] + x];
-  }
   p->h_items.resize(T.n_items);
   for (int32_t x = 0; x < T.n_items; ++x) {
     const int32_t gi = T.items[5 * x], r0 = T.items[5 * x + 1], nr = T.items[5 * x + 2],
@@ -143,10 +150,7 @@ void device_forms(ta_plan* p) {
     w.tok1 = T.chunks[3 * ci + 2];
     w.seg_base = T.group_seg_base[gi];
     w.slot0 = G[7] + (ci - G[5]) * G[3];
-    int64_t min_vis = INT64_MAX;
-    for (int32_t qig = r0 / p->g; qig <= (r0 + nr - 1) / p->g; ++qig)
-      min_vis = std::min(min_vis, q_vis[T.group_qs[G[4] + qig]]);
-    w.flags = min_vis < ta::kHiLoMinPath ? 1 : 0;
+    w.flags = 0;
     p->h_items[x] = w;
   }
   // per slot: workspace index of its q-head 0 and the q-head stride, pair-major
@@ -198,7 +202,7 @@ ta_status ensure_workspace(ta_plan* p, bool headroom, bool* moved) {
   if (p->d_ws) (void)hipFree(p->d_ws);
   p->d_ws = nullptr;
   const int64_t cap = headroom ? 2 * p->ws_bytes : p->ws_bytes;
-  hipError_t e = hipMalloc(&p->d_ws, size_t(cap));
+  hipError_t e = alloc_fails(p) ? hipErrorOutOfMemory : hipMalloc(&p->d_ws, size_t(cap));
   if (e != hipSuccess) {
     p->d_ws = nullptr;
     p->ws_cap = 0;
@@ -235,7 +239,7 @@ ta_status upload_full(ta_plan* p, bool headroom, bool* moved) {
       p->reg_off[x] = total;
       total += p->reg_cap[x];
     }
-    hipError_t e = hipMalloc(&p->d_tables, total * 4);
+    hipError_t e = alloc_fails(p) ? hipErrorOutOfMemory : hipMalloc(&p->d_tables, total * 4);
     if (e != hipSuccess) {
       p->d_tables = nullptr;
       return set_err(TA_ENOMEM, std::string("tree_attn_plan: hipMalloc(tables): ") + hipGetErrorString(e));
@@ -330,7 +334,9 @@ ta_status upload_incremental(ta_plan* p, hipStream_t s, const ta::AppendArgs* ap
     if (p->h_stage[b]) (void)hipHostFree(p->h_stage[b]);
     p->h_stage[b] = nullptr;
     const size_t cap = align64w(std::max(2 * words, p->tables_words));
-    if ((e = hipHostMalloc(reinterpret_cast<void**>(&p->h_stage[b]), cap * 4, hipHostMallocDefault)) != hipSuccess) {
+    e = alloc_fails(p) ? hipErrorOutOfMemory
+                       : hipHostMalloc(reinterpret_cast<void**>(&p->h_stage[b]), cap * 4, hipHostMallocDefault);
+    if (e != hipSuccess) {
       p->h_stage[b] = nullptr;
       p->h_stage_cap[b] = 0;
       return hip_err(e, "tree_attn_plan_extend: hipHostMalloc(staging)");
@@ -359,7 +365,10 @@ ta_status upload_incremental(ta_plan* p, hipStream_t s, const ta::AppendArgs* ap
 // a launch of its own after them.
 ta_status extend_impl(ta_plan* plan, const int32_t* leaf_add, const int32_t* new_pages, int64_t n_new_pages,
                       void* hip_stream, int32_t* relaunch, const ta::AppendArgs* app) {
+  bool changed = false;  // the plan's state has moved on: a failure from here leaves it unusable
   try {
+    if (!plan->usable)
+      return set_err(TA_EINVAL, "tree_attn_plan_extend: the plan is unusable after a failed update");
     if (!plan->host_only) {
       int dev = -1;
       hipError_t e = hipGetDevice(&dev);
@@ -367,10 +376,12 @@ ta_status extend_impl(ta_plan* plan, const int32_t* leaf_add, const int32_t* new
       if (dev != plan->device)
         return set_err(TA_EINVAL, "tree_attn_plan_extend: current device differs from the plan's");
     }
+    if (alloc_fails(plan)) throw std::bad_alloc();  // testing: the host step (plan unchanged)
     const int32_t old_items = plan->T.n_items, old_stream = plan->T.n_stream_items, old_slots = plan->T.n_slots;
     std::string err;
     const int rc = ta::plan_extend(plan->S, leaf_add, new_pages, n_new_pages, &err);
     if (rc != 0) return set_err(ta_status(rc), err);
+    changed = true;
     ta::plan_layout(plan->S, plan->T);
     if (plan->host_only) return TA_OK;
     size_t need[6];
@@ -392,7 +403,10 @@ ta_status extend_impl(ta_plan* plan, const int32_t* leaf_add, const int32_t* new
       st = upload_full(plan, true, &moved);
       plan->sized_for_growth = true;
     }
-    if (st != TA_OK) return st;
+    if (st != TA_OK) {
+      plan->usable = false;
+      return st;
+    }
     if (app && !app_done) {
       const hipError_t e = ta::launch_append(*app, static_cast<hipStream_t>(hip_stream));
       if (e != hipSuccess) return hip_err(e, "tree_attn_plan_extend_append: append launch");
@@ -402,6 +416,7 @@ ta_status extend_impl(ta_plan* plan, const int32_t* leaf_add, const int32_t* new
                    plan->T.n_slots != old_slots) ? 1 : 0;
     return TA_OK;
   } catch (const std::bad_alloc&) {
+    if (changed) plan->usable = false;
     return set_err(TA_ENOMEM, "tree_attn_plan_extend: host allocation failed");
   }
 }
@@ -443,6 +458,30 @@ ta_status append_args(const char* fn, const ta_paged_kv* kv, const void* k_new, 
   return TA_OK;
 }
 
+// TREE_ATTN_LOG set (and not "0"): one line of plan statistics on stderr per
+// tree_attn_plan: groups, joined edges, chunks, items by class, partial
+// slots, the split's chunk length, workspace bytes, unique K/V tokens and the
+// partial-result bytes one decode writes and reads back.
+void log_plan(const ta_plan* p) {
+  const char* env = std::getenv("TREE_ATTN_LOG");
+  if (!env || !*env || std::strcmp(env, "0") == 0) return;
+  const ta::PlanTables& T = p->T;
+  int32_t joined = 0;
+  for (size_t v = 0; v < T.edges.size(); ++v) joined += T.edges[v];
+  const int64_t pair_bytes = int64_t(p->head_dim + 2) * 4;
+  const int64_t partial = 2 * int64_t(T.n_slots) * p->n_qheads * pair_bytes;
+  const int64_t ws = p->host_only ? int64_t(align256(size_t(T.n_slots) * p->n_qheads * p->head_dim * 4)) +
+                                        2 * int64_t(align256(size_t(T.n_slots) * p->n_qheads * 4))
+                                  : p->ws_bytes;
+  std::fprintf(stderr,
+               "tree_attn_plan: nodes %d queries %d groups %d edges_joined %d chunks %d items %d "
+               "(workgroup %d single_wave %d) slots %d chunk_tokens %d workspace_bytes %lld "
+               "kv_tokens %lld partial_bytes %lld\n",
+               p->S.n, T.n_queries, T.n_groups, joined, T.n_chunks, T.n_items, T.n_items - T.n_stream_items,
+               T.n_stream_items, T.n_slots, T.params.size() > 22 ? T.params[22] : 0, (long long)ws,
+               (long long)p->S.total_tokens, (long long)partial);
+}
+
 }  // namespace
 
 extern "C" {
@@ -476,7 +515,10 @@ ta_status tree_attn_plan(const int32_t* parent, int32_t n_nodes, const int32_t* 
       if (opts->stream_rows) pp.stream_rows = opts->stream_rows < 0 ? 0 : opts->stream_rows;
       if (opts->split_align) pp.split_align = opts->split_align;
       pp.tile_join = opts->no_tile_join ? 0 : 1;
+      if (opts->fail_alloc_after < 0) return set_err(TA_EINVAL, "tree_attn_plan: negative fail_alloc_after");
     }
+    const int32_t fail_after = opts ? opts->fail_alloc_after : 0;
+    if (fail_after == 1) return set_err(TA_ENOMEM, "tree_attn_plan: host allocation failed (plan)");
     int device = -1;
     if (!host_only) {
       hipError_t e = hipGetDevice(&device);
@@ -490,7 +532,10 @@ ta_status tree_attn_plan(const int32_t* parent, int32_t n_nodes, const int32_t* 
     }
     if (!(scale >= 0.0f) || std::isinf(scale)) return set_err(TA_EINVAL, "tree_attn_plan: bad scale");
     p = new ta_plan;
+    p->fail_after = fail_after;
+    p->alloc_steps = 1;  // the plan object
     std::string err;
+    if (alloc_fails(p)) throw std::bad_alloc();  // testing: the planner state
     const int rc = ta::plan_init(parent, n_nodes, node_kv_len, node_page_ptr, node_page_ids,
                                  page_size, queries_per_leaf, n_qheads, n_kvheads, head_dim, pp,
                                  &p->S, &err);
@@ -498,6 +543,7 @@ ta_status tree_attn_plan(const int32_t* parent, int32_t n_nodes, const int32_t* 
       delete p;
       return set_err(ta_status(rc), err);
     }
+    if (alloc_fails(p)) throw std::bad_alloc();  // testing: the tables
     ta::plan_layout(p->S, p->T);
     p->host_only = host_only;
     p->head_dim = head_dim;
@@ -517,6 +563,7 @@ ta_status tree_attn_plan(const int32_t* parent, int32_t n_nodes, const int32_t* 
         return s;
       }
     }
+    log_plan(p);
     *out_plan = p;
     return TA_OK;
   } catch (const std::bad_alloc&) {
@@ -559,6 +606,7 @@ ta_status tree_attn_decode(const void* q, ta_dtype q_dtype, const ta_paged_kv* k
   g_err.clear();
   if (!plan) return set_err(TA_EINVAL, "tree_attn_decode: plan is NULL");
   if (plan->host_only) return set_err(TA_EINVAL, "tree_attn_decode: plan was built host_only");
+  if (!plan->usable) return set_err(TA_EINVAL, "tree_attn_decode: the plan is unusable after a failed update");
   if (!q || !kv || !out || !kv->k || !kv->v)
     return set_err(TA_EINVAL, "tree_attn_decode: NULL pointer argument");
   if (q_dtype != TA_F32 && q_dtype != TA_BF16)

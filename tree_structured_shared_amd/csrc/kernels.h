@@ -17,14 +17,8 @@ struct WorkItem {
   int32_t tok1;      // chunk end (exclusive)
   int32_t seg_base;  // offset of the group's segment in seg_tok
   int32_t slot0;     // slot of the chunk's first group query: slot_base + chunk * n_q
-  int32_t flags;     // bit 0: P enters P V as a bf16 hi + lo pair (some query of the
-                     // item sees fewer than kHiLoMinPath tokens in total)
+  int32_t flags;     // reserved (0)
 };
-
-// Below this many visible tokens (over a query's whole path) the rounding of
-// the softmax weights to bf16 before the P V product is no longer averaged
-// away, so such queries get the exact two-term (hi + lo) product.
-constexpr int32_t kHiLoMinPath = 1024;
 
 // LDS stages of the workgroup tile loop (17 KiB each at head_dim 128: K, V
 // and page-table words of 32 tokens; the loop keeps kLdsStages - 1 tiles in

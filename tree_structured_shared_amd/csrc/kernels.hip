@@ -65,6 +65,10 @@ constexpr int kBlock = 256;
 constexpr int kWaves = 4;
 constexpr int kBlockRowTiles = 2; // 16-row tiles per wave in workgroup items
 constexpr float kRescale = 8.0f;  // lazy-rescale threshold, log2 units
+// a row tile's weights enter P V as a bf16 hi + lo pair when some row's
+// largest weight of the tile exceeds this share of its running sum
+// (including the tile)
+constexpr float kLoFrac = 0.125f;
 // initial running max of the MFMA path: finite, so exp2(s - m) of a masked
 // score (-inf) is 0 even before any score was seen, with no extra guard;
 // exp2(kMInit - anything finite) is 0, so the first real max replaces it.
@@ -152,23 +156,24 @@ __device__ __forceinline__ float part_weight(float m, float M) {
 // ---------------------------------------------------------------------------
 // Rows of a work item. Row rr of the item is group row row0 + rr = (group
 // query qig, q-head-in-group hig); its partial goes to slot slot0 + qig, stored
-// at that slot's workspace index for the row's q-head (pair-major layout).
+// at that slot's workspace index for the row's q-head (pair-major layout):
+// pi = slot_pos[2 s] + qh * slot_pos[2 s + 1], below 2^31 (the host checks
+// slots x q-heads against it). Only vis, pi and ok stay live over the tile
+// loop; gq and qh serve the Q load.
 struct RowRef {
-  int gq, vis, qh;
-  int pbase, pstride;  // workspace index of this row's partial: pbase + qh * pstride
+  int gq, vis, qh, pi;
   bool ok;
 };
 
 __device__ __forceinline__ RowRef row_ref(const PartialArgs& a, const WorkItem& it, int h, int rr) {
-  RowRef r{0, 0, 0, 0, 0, rr < it.nrows};
+  RowRef r{0, 0, 0, 0, rr < it.nrows};
   if (r.ok) {
     const int grow = it.row0 + rr;
     const int qig = grow / a.g, hig = grow - qig * a.g;
     r.gq = a.group_qs[it.q_ptr + qig];
     r.vis = a.group_vis[it.q_ptr + qig];
-    r.pbase = a.slot_pos[2 * (it.slot0 + qig)];
-    r.pstride = a.slot_pos[2 * (it.slot0 + qig) + 1];
     r.qh = h * a.g + hig;
+    r.pi = a.slot_pos[2 * (it.slot0 + qig)] + r.qh * a.slot_pos[2 * (it.slot0 + qig) + 1];
   }
   return r;
 }
@@ -371,7 +376,9 @@ __device__ __forceinline__ void valu_write(const ValuState<T, D, R>& S, const Pa
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     if (!S.row[r].ok) continue;
-    const int64_t pi = int64_t(S.row[r].pbase) + int64_t(S.row[r].qh) * S.row[r].pstride;
+    int32_t pi32 = S.row[r].pi;
+    asm volatile("" : "+v"(pi32));  // keep the 32-bit index live over the loop, widen here
+    const int64_t pi = pi32;
     float* op = a.o_part + pi * D + lane * EPL;
 #pragma unroll
     for (int k4 = 0; k4 < EPL / 4; ++k4)
@@ -503,42 +510,51 @@ __device__ __forceinline__ void load_tile_kv(TileKV<D>& b, const TileSeg& sg, co
   for (int e = 0; e < 8; ++e) b.v[e].load(vb, TokOff<FA>::of(seg_of(sg, tau(j, e)), a) + Off(i * DPL * 2));
 }
 
-// softmax of one row tile's 32 scores: raises the running max when needed,
-// rescales l and O, and returns the weights as MFMA B operands. Tokens at or
-// past lim are masked (skipped, wave-uniformly, when the whole tile is
-// visible to every row of the tile). HILO: P = P_hi + P_lo,
-// both bf16, so the P V product keeps ~16 mantissa bits of P; otherwise P is
-// rounded once to bf16 and l sums the rounded weights, so the output stays
-// an exact weighted average of V.
-// With LMF the caller sums l on the matrix cores (ones x P^T into S.L4)
-// instead of here.
-template <int D, int NRTW, bool HILO, bool LMF = false>
-__device__ __forceinline__ void mfma_softmax(MfmaState<D, NRTW>& S, int k, const f32x4& s0, const f32x4& s1,
-                                             const PartialArgs& a, const WorkItem& it, int base, int j,
-                                             bf16x8& pb, bf16x8& pl) {
+// Softmax of one row tile's 32 scores.
+//
+// mfma_softmax_max: masks tokens at or past the row's limit (the score
+// accumulators s0, s1 are rewritten in place; skipped, wave-uniformly, when
+// the whole tile is visible to every row of the tile), raises the running
+// max when needed (rescaling l and O) and returns the row's largest weight
+// of the tile, exp2(tile max - running max).
+//
+// mfma_softmax_weights<SPLIT>: the weights as MFMA B operands, each rounded
+// once to bf16 (pb) or, SPLIT, as a bf16 pair pb + pl (~16 bits of P);
+// without LMF it also adds to the lane-partial S.l the weights exactly as
+// P V uses them (pb, or p when split), so the output stays a weighted
+// average of V. (With LMF the caller sums l on the matrix cores, ones x P^T
+// into S.L4.)
+//
+// Precision of the P V product. Rounding a weight w to bf16 moves the
+// output by up to 2^-8 w |v - o| / L (L the row's final sum of weights).
+// Weights that are each a small share of L round independently and their
+// errors average out; a few dominant ones (an attention sink, two near-equal
+// peaks) do not. So a row tile's weights enter P V split into hi + lo
+// whenever some row's largest weight of the tile exceeds kLoFrac of that
+// row's running sum l including the tile (split_needed): the sums only grow
+// (in the scale of the current max), so every weight left single-rounded is
+// at most kLoFrac of L. The decision is a ballot over the wave.
+template <int D, int NRTW>
+__device__ __forceinline__ float mfma_softmax_max(MfmaState<D, NRTW>& S, int k, f32x4& s0, f32x4& s1,
+                                                  const PartialArgs& a, const WorkItem& it, int base, int j) {
   constexpr int DPL = D / 16;
   const float c = a.scale_log2;
-  float sv[8];
-#pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    sv[x] = s0[x];
-    sv[4 + x] = s1[x];
-  }
   if (base + 32 > min(it.tok1, S.vmin[k])) {  // wave-uniform: some token of the tile is masked
-    const int lim = min(it.tok1, S.row[k].vis) - base;
+    // tokens 4 j + x and 16 + 4 j + x of the tile against the row's limit
+    const int lim = min(it.tok1, S.row[k].vis) - base - 4 * j;
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
-      if (4 * j + x >= lim) sv[x] = TA_NEG_INF;
-      if (16 + 4 * j + x >= lim) sv[4 + x] = TA_NEG_INF;
+      if (x >= lim) s0[x] = TA_NEG_INF;
+      if (16 + x >= lim) s1[x] = TA_NEG_INF;
     }
   }
-  // four three-input maxes (sv[0] enters twice to make nine operands):
+  // four three-input maxes (s0[0] enters twice to make nine operands):
   // v_max3_f32 takes the matrix-core results as they are, where a tree of
   // two-input maxes first quiets each operand with an instruction of its own
-  float mx = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
-  mx = fmaxf(fmaxf(mx, sv[3]), sv[4]);
-  mx = fmaxf(fmaxf(mx, sv[5]), sv[6]);
-  mx = fmaxf(fmaxf(mx, sv[7]), sv[0]);
+  float mx = fmaxf(fmaxf(s0[0], s0[1]), s0[2]);
+  mx = fmaxf(fmaxf(mx, s0[3]), s1[0]);
+  mx = fmaxf(fmaxf(mx, s1[1]), s1[2]);
+  mx = fmaxf(fmaxf(mx, s1[3]), s0[0]);
   mx = max4rows(mx) * c;  // c > 0: the max of scaled scores
   const bool raise = mx > S.m[k] + kRescale;
   if (__builtin_amdgcn_ballot_w64(raise)) {  // rare after the first tiles
@@ -549,37 +565,42 @@ __device__ __forceinline__ void mfma_softmax(MfmaState<D, NRTW>& S, int k, const
     for (int db = 0; db < DPL; ++db) S.O[k][db] *= al;
     S.m[k] = raise ? mx : S.m[k];
   }
-  const float nm = -S.m[k];
-  float p[8];
-  float psum_r = 0.0f;
+  return fast_exp2(mx - S.m[k]);
+}
+
+// wave-uniform: some row's largest weight of the tile is above kLoFrac of
+// its running sum l (this tile included)
+__device__ __forceinline__ bool split_needed(float pmax, float l) {
+  return __builtin_amdgcn_ballot_w64(pmax > kLoFrac * l) != 0;
+}
+
+template <int D, int NRTW, bool SPLIT, bool LMF = false>
+__device__ __forceinline__ void mfma_softmax_weights(MfmaState<D, NRTW>& S, int k, const f32x4& s0,
+                                                     const f32x4& s1, const PartialArgs& a, bf16x8& pb,
+                                                     bf16x8& pl) {
+  const float c = a.scale_log2, nm = -S.m[k];
+  float psum = 0.0f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    p[e] = fast_exp2(__builtin_fmaf(sv[e], c, nm));
-    pb[e] = __bf16(p[e]);
-    if constexpr (!LMF) psum_r += float(pb[e]);
-  }
-  if constexpr (HILO) {
-    float psum = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if constexpr (!LMF) psum += p[e];
-      pl[e] = __bf16(p[e] - float(pb[e]));
+    const float p = fast_exp2(__builtin_fmaf(e < 4 ? s0[e] : s1[e - 4], c, nm));
+    pb[e] = __bf16(p);
+    if constexpr (SPLIT) {
+      pl[e] = __bf16(p - float(pb[e]));
+      if constexpr (!LMF) psum += p;
+    } else if constexpr (!LMF) {
+      psum += float(pb[e]);
     }
-    if constexpr (!LMF) S.l[k] += psum;
-  } else if constexpr (!LMF) {
-    S.l[k] += psum_r;
   }
+  if constexpr (!LMF) S.l[k] += psum;
 }
 
-// O^T[db] += V^T[db] P^T (and the lo half of P when hilo)
-template <int D, int NRTW, bool HILO>
-__device__ __forceinline__ void pv_update(MfmaState<D, NRTW>& S, int k, int db, const bf16x8& vt, const bf16x8& pb,
-                                          const bf16x8& pl) {
+// O^T[db] += V^T[db] P^T
+template <int D, int NRTW>
+__device__ __forceinline__ void pv_update(MfmaState<D, NRTW>& S, int k, int db, const bf16x8& vt, const bf16x8& pb) {
   S.O[k][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pb, S.O[k][db], 0, 0, 0);
-  if constexpr (HILO) S.O[k][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pl, S.O[k][db], 0, 0, 0);
 }
 
-template <int D, int NRTW, bool HILO>
+template <int D, int NRTW>
 __device__ __forceinline__ void mfma_tile(MfmaState<D, NRTW>& S, const TileKV<D>& b, const PartialArgs& a,
                                           const WorkItem& it, int base, int j) {
   constexpr int KK = D / 32, DPL = D / 16;
@@ -605,9 +626,18 @@ __device__ __forceinline__ void mfma_tile(MfmaState<D, NRTW>& S, const TileKV<D>
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b.k[1][kk]), S.qf[k][kk], s1, 0, 0, 0);
     }
     bf16x8 pb, pl;
-    mfma_softmax<D, NRTW, HILO>(S, k, s0, s1, a, it, base, j, pb, pl);
+    const float pmax = mfma_softmax_max<D, NRTW>(S, k, s0, s1, a, it, base, j);
+    const float l0 = S.l[k];
+    mfma_softmax_weights<D, NRTW, false>(S, k, s0, s1, a, pb, pl);
+    if (split_needed(pmax, sum4rows(S.l[k]))) {  // the weights again, split; l takes them unrounded
+      S.l[k] = l0;
+      mfma_softmax_weights<D, NRTW, true>(S, k, s0, s1, a, pb, pl);
 #pragma unroll
-    for (int db = 0; db < DPL; ++db) pv_update<D, NRTW, HILO>(S, k, db, vt[db], pb, pl);
+      for (int db = 0; db < DPL; ++db)
+        S.O[k][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[db], pl, S.O[k][db], 0, 0, 0);
+    }
+#pragma unroll
+    for (int db = 0; db < DPL; ++db) pv_update<D, NRTW>(S, k, db, vt[db], pb);
   }
 }
 
@@ -616,7 +646,7 @@ __device__ __forceinline__ void mfma_tile(MfmaState<D, NRTW>& S, const TileKV<D>
 // counter is concerned, so every tile's page-table entries are requested
 // before the K/V of the tile ahead of it: waiting for them then never waits
 // for younger K/V data, and two tiles stay in flight while one is computed.
-template <int D, int NRTW, bool FA, bool HILO>
+template <int D, int NRTW, bool FA>
 __device__ __forceinline__ void mfma_stream(MfmaState<D, NRTW>& S, const PartialArgs& a, const WorkItem& it,
                                             int h, TileSeg sgA, TileSeg sgB) {
   const int lane = threadIdx.x & 63;
@@ -639,10 +669,10 @@ __device__ __forceinline__ void mfma_stream(MfmaState<D, NRTW>& S, const Partial
   // compiler drain every load at the back edge): the second half is skipped
   // wave-uniformly on an odd last tile
   for (int kt = 0; kt < ntiles; kt += 2, base += 64) {
-    mfma_tile<D, NRTW, HILO>(S, bA, a, it, base, j);
+    mfma_tile<D, NRTW>(S, bA, a, it, base, j);
     load_tile_kv<D, FA>(bA, sgA, kb, vb, j, i, a);
     load_tile_seg(sgA, st, base + 128, last, i, j);
-    if (kt + 1 < ntiles) mfma_tile<D, NRTW, HILO>(S, bB, a, it, base + 32, j);
+    if (kt + 1 < ntiles) mfma_tile<D, NRTW>(S, bB, a, it, base + 32, j);
     load_tile_kv<D, FA>(bB, sgB, kb, vb, j, i, a);
     load_tile_seg(sgB, st, base + 160, last, i, j);
   }
@@ -663,7 +693,9 @@ __device__ __forceinline__ void mfma_write(MfmaState<D, NRTW>& S, const PartialA
     if (!S.on[k]) continue;
     const float l = LM ? S.L4[k][0] : sum4rows(S.l[k]);
     if (!S.row[k].ok) continue;
-    const int64_t pi = int64_t(S.row[k].pbase) + int64_t(S.row[k].qh) * S.row[k].pstride;
+    int32_t pi32 = S.row[k].pi;
+    asm volatile("" : "+v"(pi32));  // keep the 32-bit index live over the loop, widen here
+    const int64_t pi = pi32;
     if constexpr (TR) {
       float* op = a.o_part + pi * D + 4 * j;
 #pragma unroll
@@ -700,8 +732,7 @@ __device__ __forceinline__ void mfma_wave(const PartialArgs& a, const WorkItem& 
   load_tile_seg(sgB, a.seg_tok + it.seg_base, it.tok0 + 32, it.tok1 - 1, lane & 15, lane >> 4);
   MfmaState<D, NRTW> S;
   mfma_init(S, a, it, h, rt, on);
-  if (it.flags & 1) mfma_stream<D, NRTW, FA, true>(S, a, it, h, sgA, sgB);
-  else mfma_stream<D, NRTW, FA, false>(S, a, it, h, sgA, sgB);
+  mfma_stream<D, NRTW, FA>(S, a, it, h, sgA, sgB);
   mfma_write(S, a);
 }
 
@@ -827,7 +858,7 @@ struct TileDma {
 // One tile for the wave's first NACT row tiles, operands read straight from
 // an LDS stage: K one k-step at a time (the A operand of S^T for both token
 // blocks), then V^T one 16-wide d-block at a time by transpose reads.
-template <int D, int NRTW, int NACT, bool HILO>
+template <int D, int NRTW, int NACT>
 __device__ __forceinline__ void lds_tile(MfmaState<D, NRTW>& S, const char* stage, const PartialArgs& a,
                                          const WorkItem& it, int base, int i, int j) {
   typedef LdsTile<D> L;
@@ -845,10 +876,6 @@ __device__ __forceinline__ void lds_tile(MfmaState<D, NRTW>& S, const char* stag
       s1[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, S.qf[k][kk], s1[k], 0, 0, 0);
     }
   }
-  bf16x8 pb[NACT], pl[NACT];
-#pragma unroll
-  for (int k = 0; k < NACT; ++k)
-    mfma_softmax<D, NRTW, HILO, true>(S, k, s0[k], s1[k], a, it, base, j, pb[k], pl[k]);
   // V^T operands by LDS transpose reads: within each 16-lane group, lane L of
   // a ds_read_b64_tr_b16 receives element k = the (L % 4)-th 16-bit value at
   // the address of lane 4k + L / 4. Lane (i, j) points at token
@@ -858,8 +885,7 @@ __device__ __forceinline__ void lds_tile(MfmaState<D, NRTW>& S, const char* stag
   typedef __attribute__((address_space(3))) v4s lds_v4s;
   typedef __attribute__((address_space(3))) char lds_b;
   const lds_b* vstage = (const lds_b*)stage + L::PART;
-#pragma unroll
-  for (int db = 0; db < DPL; ++db) {
+  auto vt_of = [&](int db) {
     v4s half[2];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
@@ -868,19 +894,37 @@ __device__ __forceinline__ void lds_tile(MfmaState<D, NRTW>& S, const char* stag
       half[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_v4s*)(vstage + t * L::ROW + ((c ^ L::swz(1, t)) << 4) + 8 * (i & 1)));
     }
-    const bf16x8 vt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-    for (int k = 0; k < NACT; ++k) pv_update<D, NRTW, HILO>(S, k, db, vt, pb[k], pl[k]);
-  }
-  // l = ones x P^T: the row sums of the weights the P V product used, summed
-  // on the matrix cores in fp32 (the VALU sum they replace is 16 converts
-  // and adds per row tile)
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  // Per row tile: the max, the weights and their row sums l on the matrix
+  // cores (ones x P^T, so l is the sum of the weights P V uses, in fp32; the
+  // VALU sum it replaces is 16 converts and adds per row tile), then the
+  // split decision against l including this tile. A split tile adds its lo
+  // halves to O and l right away (V^T read for it), so they never outlive
+  // the branch; the hi halves of every row tile then share one pass of V^T
+  // reads.
   const bf16x8 ones = {__bf16(1.0f), __bf16(1.0f), __bf16(1.0f), __bf16(1.0f),
                        __bf16(1.0f), __bf16(1.0f), __bf16(1.0f), __bf16(1.0f)};
+  bf16x8 pb[NACT];
 #pragma unroll
   for (int k = 0; k < NACT; ++k) {
+    const float pmax = mfma_softmax_max<D, NRTW>(S, k, s0[k], s1[k], a, it, base, j);
+    bf16x8 pl;
+    mfma_softmax_weights<D, NRTW, false, true>(S, k, s0[k], s1[k], a, pb[k], pl);
     S.L4[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[k], S.L4[k], 0, 0, 0);
-    if constexpr (HILO) S.L4[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pl[k], S.L4[k], 0, 0, 0);
+    if (split_needed(pmax, S.L4[k][0])) {  // the weights again, split (pb as before)
+      mfma_softmax_weights<D, NRTW, true, true>(S, k, s0[k], s1[k], a, pb[k], pl);
+      S.L4[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pl, S.L4[k], 0, 0, 0);
+#pragma unroll
+      for (int db = 0; db < DPL; ++db)
+        S.O[k][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt_of(db), pl, S.O[k][db], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int db = 0; db < DPL; ++db) {
+    const bf16x8 vt = vt_of(db);
+#pragma unroll
+    for (int k = 0; k < NACT; ++k) pv_update<D, NRTW>(S, k, db, vt, pb[k]);
   }
 }
 
@@ -896,7 +940,7 @@ __device__ __forceinline__ void lds_tile(MfmaState<D, NRTW>& S, const char* stag
 // load latency other than the tiles' own is on the loop's path. Every
 // page-table read is clamped to the chunk's last token (loads past the last
 // tile fetch written K/V that the softmax never uses). NACT (row tiles this
-// wave computes) and HILO are fixed per loop.
+// wave computes) is fixed per loop.
 
 // s_waitcnt with vmcnt = n (< 16) and no wait on the other counters
 template <int N>
@@ -916,7 +960,7 @@ __device__ __forceinline__ void lds_stage_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-template <int D, bool FA, int NACT, bool HILO>
+template <int D, bool FA, int NACT>
 __device__ __forceinline__ void lds_stream(MfmaState<D, kBlockRowTiles>& S, char* lds, const PartialArgs& a,
                                            const WorkItem& it, int h, int i, int j) {
   typedef TileDma<D, FA> Dma;
@@ -987,7 +1031,7 @@ __device__ __forceinline__ void lds_stream(MfmaState<D, kBlockRowTiles>& S, char
     dma.issue(lds + SF * ST, w, a);
     dma4(st, word_off(n + 2 * AHEAD), lds_addr(SF * ST + wpos));
     if constexpr (NACT > 0)
-      lds_tile<D, kBlockRowTiles, NACT, HILO>(S, lds + SG * ST, a, it, it.tok0 + n * 32, i, j);
+      lds_tile<D, kBlockRowTiles, NACT>(S, lds + SG * ST, a, it, it.tok0 + n * 32, i, j);
   };
   static_assert(NS == 3, "the loop is unrolled over three stages");
   // wave-uniform: tile n sits in stage n mod 3
@@ -1010,7 +1054,6 @@ __device__ __forceinline__ void block_lds_item(const PartialArgs& a, char* lds, 
   const int i = lane & 15, j = lane >> 4;
   const WorkItem it = a.items[item];
   const int nrt = (it.nrows + 15) >> 4;
-  const bool hilo = it.flags & 1;
   // row tiles beyond kWaves * kBlockRowTiles take further passes over the
   // chunk (the planner's row blocks keep this to one pass)
   for (int r0 = 0; r0 < nrt; r0 += kWaves * kBlockRowTiles) {
@@ -1024,15 +1067,9 @@ __device__ __forceinline__ void block_lds_item(const PartialArgs& a, char* lds, 
     MfmaState<D, kBlockRowTiles> S;
     mfma_init(S, a, it, h, rt, on);
     // every wave takes part in the loads and barriers, computing or not
-    if (S.on[1]) {
-      if (hilo) lds_stream<D, FA, 2, true>(S, lds, a, it, h, i, j);
-      else lds_stream<D, FA, 2, false>(S, lds, a, it, h, i, j);
-    } else if (S.on[0]) {
-      if (hilo) lds_stream<D, FA, 1, true>(S, lds, a, it, h, i, j);
-      else lds_stream<D, FA, 1, false>(S, lds, a, it, h, i, j);
-    } else {
-      lds_stream<D, FA, 0, false>(S, lds, a, it, h, i, j);
-    }
+    if (S.on[1]) lds_stream<D, FA, 2>(S, lds, a, it, h, i, j);
+    else if (S.on[0]) lds_stream<D, FA, 1>(S, lds, a, it, h, i, j);
+    else lds_stream<D, FA, 0>(S, lds, a, it, h, i, j);
     // V^T came from transpose reads (d = 16 db + 4j + c), l from the matrix cores
     mfma_write<D, kBlockRowTiles, true>(S, a);
   }
