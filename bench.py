@@ -1,15 +1,19 @@
 """Benchmark: tree-structured decode attention, one decode step of one layer.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 5] [--extra-configs 2,3,4]
 
 A step is one tree_attn_decode (partial-attention kernel + log-sum-exp
-reduction) over the whole tree. The default workload is the multi-level
-shared system prompt tree (nodes per level 1/4/16, 2048/512/128 tokens per
-node, 32 q-heads / 32 kv-heads, head_dim 128, bf16, page size 16).
+reduction) over the whole tree. The headline workload is the largest one, the
+irregular random radix tree (root + 4 levels, branching U{1..8}, lognormal
+node lengths, 4 query tokens per leaf under a leaf-local causal mask, 32
+q-heads / 8 kv-heads, head_dim 128, bf16, page size 16: 0.31 GB of unique
+K/V). The same run times the other bf16 workloads (multi-level shared
+prompt, wide fan-out, skewed long context) with the same steps and reports
+them under "configs".
 
 The KV pool is replicated into enough copies (>= 1 GiB together) that each
 timed step reads a copy no cache level holds from the step before: the 256 MB
-Infinity Cache would otherwise serve the whole tree. Inputs are resident in
+Infinity Cache would otherwise serve a whole tree. Inputs are resident in
 HBM before the timed region. Prints one JSON line.
 """
 import argparse
@@ -33,36 +37,35 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "partial_kernel_traffic.json")
 
 
 def source_hash():
-    """sha256 over the library's sources (kernels, planner, C ABI): the HBM
-    counters recorded under profiles/ hold only for the sources they were
-    taken on."""
+    """sha256 over the sources that decide what the partial kernel moves:
+    the kernels and the planner that cuts their work. The HBM counters
+    recorded under profiles/ hold only for the sources they were taken on."""
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(ROOT, "tree_structured_shared_amd", "csrc", "*"))
-                   + glob.glob(os.path.join(ROOT, "include", "*.h")))
-    for f in files:
-        if f.endswith((".hip", ".cpp", ".h")):
-            h.update(os.path.basename(f).encode())
-            with open(f, "rb") as fh:
-                h.update(fh.read())
+    csrc = os.path.join(ROOT, "tree_structured_shared_amd", "csrc")
+    for name in ("kernels.hip", "kernels.h", "planner.cpp", "planner.h"):
+        h.update(name.encode())
+        with open(os.path.join(csrc, name), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()
 
 
 def _traffic(workload):
     """HBM bytes per partial-kernel launch from the recorded FETCH_SIZE /
-    WRITE_SIZE counters, each scaled by what the counter reads for a plain
-    copy of known size; None when no record matches these sources and this
-    workload."""
+    WRITE_SIZE counters of this workload, each scaled by what the counter
+    reads for a plain copy of known size; None when the record was taken on
+    other sources or holds no such workload."""
     try:
         with open(TRAFFIC_FILE) as fh:
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != source_hash() or rec.get("workload") != workload:
+    w = rec.get("workloads", {}).get(workload)
+    if rec.get("source_sha256") != source_hash() or w is None:
         return None
     cal = rec["copy_calibration"]
     f_scale = cal["bytes"] / (cal["fetch_size_kib"] * 1024.0)
     w_scale = cal["bytes"] / (cal["write_size_kib"] * 1024.0)
-    return round(rec["fetch_size_kib"] * 1024.0 * f_scale + rec["write_size_kib"] * 1024.0 * w_scale)
+    return round(w["fetch_size_kib"] * 1024.0 * f_scale + w["write_size_kib"] * 1024.0 * w_scale)
 
 
 def _copy_calibration(mib):
@@ -77,7 +80,7 @@ def _copy_calibration(mib):
     print(json.dumps({"copy_bytes": n, "copies": 3}), flush=True)
 
 
-def _cpu_baseline(inst, budget_s=12.0, max_reps=20):
+def _cpu_baseline(inst, budget_s=20.0, max_reps=20):
     """The fp64 oracle, untuned, on the host cores: whole decode steps of the
     same workload, repeated until ~budget_s of CPU work."""
     from oracle import tree_attention as oracle
@@ -314,12 +317,122 @@ def _decode_loop(args, inst, dev):
     plan.close()
 
 
+def _pools(inst, dev, copies):
+    q = inst.q.to(dev)
+    ks = [head_major_pool(inst.k_pool, dev) for _ in range(copies)]
+    vs = [head_major_pool(inst.v_pool, dev) for _ in range(copies)]
+    return q, ks, vs
+
+
+def _copies(inst, requested):
+    import torch
+    esize = 2 if inst.dtype == torch.bfloat16 else 4
+    pool_bytes = 2 * inst.k_pool.numel() * esize
+    return requested or max(2, math.ceil((1 << 30) / pool_bytes) + 1)
+
+
+def _measure(inst, plan, calls, K, W):
+    """Wall time per step over K back-to-back steps (after W warm-up steps),
+    then the same K steps with the library's per-kernel events."""
+    import numpy as np
+    import torch
+    copies = len(calls)
+    for s in range(W):
+        calls[s % copies]()
+    torch.cuda.synchronize()
+    # timed region: K back-to-back decode steps, each on its own KV copy
+    # (no collector pauses inside it)
+    gc.disable()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        calls[s % copies]()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gc.enable()
+    # per-kernel device time: the library launches each kernel with HIP
+    # start/stop events stamped at that kernel's own start and end, on the
+    # stream it runs on
+    plan.timing_enable(K)
+    for s in range(K):
+        calls[s % copies]()
+    torch.cuda.synchronize()
+    pm, rm = plan.timing_read(K)
+    plan.timing_enable(0)
+    return wall * 1e6 / K, float(np.mean(pm)) * 1e3, float(np.mean(rm)) * 1e3, pm, rm
+
+
+def _rates(inst, us_step, part_us, red_us):
+    """The metric's figures for one workload: effective GB/s over unique K/V
+    bytes per step, the dominant kernel's roofline and the MFMA rate."""
+    import torch
+    unique = inst.unique_kv_bytes
+    bf16 = inst.dtype == torch.bfloat16
+    dominant = f"partial_kernel<{'bf16' if bf16 else 'f32'},{inst.head_dim}>"
+    flops = algorithmic_flops(inst)
+    achieved = unique / (part_us * 1e-6) / 1e9
+    value = unique / (us_step * 1e-6) / 1e9
+    return {
+        "us_per_step": round(us_step, 2),
+        "effective_GBs": round(value, 2),
+        "frac_of_peak": round(value / HBM_PEAK_GBS, 4),
+        "kernels_us": {"partial_attn": round(part_us, 3), "lse_reduce": round(red_us, 3)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": _traffic(inst.name), "traffic_unit": "bytes per launch",
+                     "kernel": dominant, "kernel_us": round(part_us, 3),
+                     "alg_bytes": unique},
+        "mfma": {"alg_flops": flops, "achieved_tflops": round(flops / (part_us * 1e-6) / 1e12, 1),
+                 "peak_tflops": MFMA_BF16_PEAK_TFLOPS if bf16 else None,
+                 "frac": (round(flops / (part_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4) if bf16 else None),
+                 "kernel": dominant},
+    }
+
+
+def _plan_info(plan, inst):
+    P = plan.export("params")
+    return {"groups": int(P[18]), "chunks": int(P[19]), "items": int(P[20]), "slots": int(P[21]),
+            "units": int(P[20]) * inst.n_kvheads, "edges_joined": int(plan.export("edges").sum())}
+
+
+def _workload_desc(inst, copies):
+    return {"workload": inst.name, "n_nodes": inst.n_nodes, "n_queries": inst.n_queries,
+            "queries_per_leaf": inst.qpl, "n_qheads": inst.n_qheads, "n_kvheads": inst.n_kvheads,
+            "head_dim": inst.head_dim, "page_size": inst.page_size, "unique_kv_bytes": inst.unique_kv_bytes,
+            "kv_copies_rotated": copies}
+
+
+def _extra_config(k, args, dev):
+    """One more workload, timed like the headline (same steps and warm-up)."""
+    import torch
+
+    import synth
+    from tree_structured_shared_amd import Plan
+    inst = synth.make_config(k)
+    copies = _copies(inst, args.copies)
+    q, ks, vs = _pools(inst, dev, copies)
+    plan = Plan.for_instance(inst)
+    out = torch.empty((inst.n_queries, inst.n_qheads, inst.head_dim), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    calls = [plan.launcher(q, ks[c], vs[c], out, stream.cuda_stream) for c in range(copies)]
+    us, part, red, _, _ = _measure(inst, plan, calls, args.steps, args.warmup)
+    res = dict(_workload_desc(inst, copies), **_rates(inst, us, part, red))
+    res["plan"] = _plan_info(plan, inst)
+    plan.close()
+    del calls, ks, vs, q, out
+    gc.collect()
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--config", type=int, default=5)
+    ap.add_argument("--extra-configs", default="2,3,4",
+                    help="comma-separated workloads timed after the headline one ('' for none)")
     ap.add_argument("--copies", type=int, default=0, help="KV pool copies (0 = enough for 1 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -348,19 +461,14 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     inst = synth.make_config(args.config)
-    unique = inst.unique_kv_bytes
-    esize = 2 if inst.dtype == torch.bfloat16 else 4
-    pool_bytes = 2 * inst.k_pool.numel() * esize
-    copies = args.copies or max(2, math.ceil((1 << 30) / pool_bytes) + 1)
+    copies = _copies(inst, args.copies)
 
     if args.decode_loop:
         _decode_loop(args, inst, dev)
         return
 
     if args.ablation:
-        q = inst.q.to(dev)
-        ks = [head_major_pool(inst.k_pool, dev) for _ in range(copies)]
-        vs = [head_major_pool(inst.v_pool, dev) for _ in range(copies)]
+        q, ks, vs = _pools(inst, dev, copies)
         _ablation(args, inst, q, ks, vs, dev)
         return
 
@@ -373,39 +481,14 @@ def main():
     t0 = time.perf_counter()
     plan = Plan.for_instance(inst)
     t_plan_full = time.perf_counter() - t0
-    P = plan.export("params")
 
-    q = inst.q.to(dev)
-    ks = [head_major_pool(inst.k_pool, dev) for _ in range(copies)]
-    vs = [head_major_pool(inst.v_pool, dev) for _ in range(copies)]
+    q, ks, vs = _pools(inst, dev, copies)
     out = torch.empty((inst.n_queries, inst.n_qheads, inst.head_dim), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     calls = [plan.launcher(q, ks[c], vs[c], out, stream.cuda_stream) for c in range(copies)]
-
-    for s in range(args.warmup):
-        calls[s % copies]()
-    torch.cuda.synchronize()
-
     K = args.steps
-    # timed region: K back-to-back decode steps, each on its own KV copy
-    # (no collector pauses inside it)
-    gc.disable()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(K):
-        calls[s % copies]()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gc.enable()
+    us_step, part_us, red_us, pm, rm = _measure(inst, plan, calls, K, args.warmup)
     ref_out = out.clone()
-
-    # per-kernel device time: the library launches each kernel with HIP
-    # start/stop events stamped at that kernel's own start and end
-    plan.timing_enable(K)
-    for s in range(K):
-        calls[s % copies]()
-    torch.cuda.synchronize()
-    pm, rm = plan.timing_read(K)
 
     # warm reference: the same copy every step (Infinity Cache may hold it)
     plan.timing_enable(K)
@@ -438,6 +521,7 @@ def main():
         g.replay()
         torch.cuda.synchronize()
         graph_us = (time.perf_counter() - t0) * 1e6 / K
+        del g, gcalls
     except Exception as exc:  # reported, never silently folded into value
         graph_us = f"unavailable: {exc}"
 
@@ -456,65 +540,50 @@ def main():
     token_major_us = (time.perf_counter() - t0) * 1e6 / K
     if not torch.allclose(out, ref_out, rtol=0.0, atol=1e-5):
         raise RuntimeError("token-major pools give a different output")
-    del tcalls, tk, tv
+    plan_desc = _plan_info(plan, inst)
+    plan.close()
+    del tcalls, tk, tv, calls, ks, vs
+    gc.collect()
+    torch.cuda.empty_cache()
 
-    ms_per_step = wall * 1e3 / K
-    part_us = float(np.mean(pm)) * 1e3
-    red_us = float(np.mean(rm)) * 1e3
-    dominant = f"partial_kernel<{'bf16' if inst.dtype == torch.bfloat16 else 'f32'},{inst.head_dim}>"
-    value = unique / (ms_per_step * 1e-3) / 1e9
-    flops = algorithmic_flops(inst)
-    achieved = unique / (part_us * 1e-6) / 1e9
+    rates = _rates(inst, us_step, part_us, red_us)
+    value = rates["effective_GBs"]
     res = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": value,
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "us_per_step": round(ms_per_step * 1e3, 2),
-        "frac_of_peak": round(value / HBM_PEAK_GBS, 4),
+        "ms_per_step": round(us_step * 1e-3, 5),
+        "us_per_step": rates["us_per_step"],
+        "frac_of_peak": rates["frac_of_peak"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if inst.dtype == torch.bfloat16 else "f32",
         "data": "synthetic",
-        "config": {
-            "workload": inst.name,
-            "n_nodes": inst.n_nodes,
-            "n_queries": inst.n_queries,
-            "queries_per_leaf": inst.qpl,
-            "n_qheads": inst.n_qheads,
-            "n_kvheads": inst.n_kvheads,
-            "head_dim": inst.head_dim,
-            "page_size": inst.page_size,
-            "unique_kv_bytes": unique,
-            "kv_copies_rotated": copies,
-            "pool_layout": "head-major pages: storage [n_pages, n_kvheads, page_size, head_dim]",
-            "plan": {"groups": int(P[18]), "chunks": int(P[19]), "items": int(P[20]),
-                     "slots": int(P[21]), "units": int(P[20]) * inst.n_kvheads,
-                     "edges_joined": int(plan.export("edges").sum())},
-        },
-        "kernels_us": {"partial_attn": round(part_us, 3), "lse_reduce": round(red_us, 3),
-                       "device_step": round(float(np.mean(pm + rm)) * 1e3, 3),
-                       "partial_attn_warm": round(float(np.mean(pm_w)) * 1e3, 3),
-                       "lse_reduce_warm": round(float(np.mean(rm_w)) * 1e3, 3)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": _traffic(inst.name), "traffic_unit": "bytes per launch",
-                     "kernel": dominant, "kernel_us": round(part_us, 3)},
-        "mfma": {"alg_flops": flops, "achieved_tflops": round(flops / (part_us * 1e-6) / 1e12, 1),
-                 "peak_tflops": MFMA_BF16_PEAK_TFLOPS if inst.dtype == torch.bfloat16 else None,
-                 "frac": (round(flops / (part_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
-                          if inst.dtype == torch.bfloat16 else None),
-                 "kernel": dominant},
+        "config": dict(_workload_desc(inst, copies),
+                       pool_layout="head-major pages: storage [n_pages, n_kvheads, page_size, head_dim]",
+                       plan=plan_desc),
+        "kernels_us": dict(rates["kernels_us"], device_step=round(float(np.mean(pm + rm)) * 1e3, 3),
+                           partial_attn_warm=round(float(np.mean(pm_w)) * 1e3, 3),
+                           lse_reduce_warm=round(float(np.mean(rm_w)) * 1e3, 3)),
+        "roofline": rates["roofline"],
+        "mfma": rates["mfma"],
         "graph_us_per_step": round(graph_us, 3) if isinstance(graph_us, float) else graph_us,
         "token_major_pool_us_per_step": round(token_major_us, 2),
         "planner_host_ms": {"tables_median": round(statistics.median(t_host) * 1e3, 3),
                             "with_upload": round(t_plan_full * 1e3, 3)},
     }
-    plan.close()
+    extra = [int(x) for x in args.extra_configs.split(",") if x.strip()] if args.extra_configs else []
+    if extra:
+        res["configs"] = {}
+        for k in extra:
+            if k == args.config:
+                continue
+            r = _extra_config(k, args, dev)
+            res["configs"][r["workload"]] = r
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = _cpu_baseline(inst)
     print(json.dumps(res), flush=True)

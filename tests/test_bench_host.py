@@ -48,14 +48,16 @@ def test_traffic_record_only_for_its_sources_and_workload():
     with open(b.TRAFFIC_FILE) as fh:
         rec = json.load(fh)
     assert b._traffic("no_such_workload") is None
-    got = b._traffic(rec["workload"])
-    if rec["source_sha256"] != b.source_hash():
-        assert got is None
-    else:
-        cal = rec["copy_calibration"]
-        want = (rec["fetch_size_kib"] * cal["bytes"] / cal["fetch_size_kib"]
-                + rec["write_size_kib"] * cal["bytes"] / cal["write_size_kib"])
-        assert abs(got - want) <= 1
+    assert rec["workloads"]
+    for name, w in rec["workloads"].items():
+        got = b._traffic(name)
+        if rec["source_sha256"] != b.source_hash():
+            assert got is None
+        else:
+            cal = rec["copy_calibration"]
+            want = (w["fetch_size_kib"] * cal["bytes"] / cal["fetch_size_kib"]
+                    + w["write_size_kib"] * cal["bytes"] / cal["write_size_kib"])
+            assert abs(got - want) <= 1
 
 
 def test_more_than_one_gpu_is_refused():
