@@ -186,12 +186,23 @@ ta_status tree_attn_plan_extend_append(ta_plan* plan, const int32_t* leaf_add, c
                                        const void* v_new, int64_t n_tokens, const int32_t* dst, void* hip_stream,
                                        int32_t* relaunch);
 
-/* Plan sizes. Any output pointer may be NULL. */
+/* Plan sizes. Any output pointer may be NULL. The plan owns its scratch (the
+ * fp32 partial workspace) and reports its size here: a caller never supplies
+ * or keeps scratch buffers whose size the API leaves unstated, one reason the
+ * TGI PR "Move to FlashDecoding instead of PagedAttention kernel" gives for
+ * passing over another paged-attention library. */
 ta_status tree_attn_plan_info(const ta_plan* plan, int32_t* n_queries, int64_t* workspace_bytes,
                               int32_t* n_items);
 
 /* Export one plan table as int32 (table ids below). With dst == NULL only
- * *len (element count) is written; otherwise dst must hold *len elements. */
+ * *len (element count) is written; otherwise dst must hold *len elements.
+ * The tables are the plan's whole decision (the context-query groups of the
+ * FastTree review, section 3.1, the edge assignment of its Algorithm 1, the
+ * chunks of section 3.3), exported so that they can be checked against an
+ * independent re-derivation bit for bit. They are built once per plan and
+ * reused by every decode: in the same TGI PR, building the sequence-length
+ * index tensors anew on every call cost enough to make the new path slower
+ * than the old one. */
 ta_status tree_attn_plan_export(const ta_plan* plan, int32_t table_id, int32_t* dst, int64_t* len);
 
 /* Timing of the last decodes (testing and benchmarking). After
