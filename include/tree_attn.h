@@ -128,6 +128,20 @@ ta_status tree_attn_plan(const int32_t* parent, int32_t n_nodes, const int32_t* 
 ta_status tree_attn_decode(const void* q, ta_dtype q_dtype, const ta_paged_kv* kv,
                            const ta_plan* plan, float* out, void* hip_stream);
 
+/* tree_attn_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and results, with the partial results in a static device
+ * array of 48 MiB (one per GPU, held until the process ends) instead of the
+ * plan's workspace. The call allocates nothing. Arguments, layouts and
+ * asynchrony as in tree_attn_decode. TA_EINVAL when the plan's partial
+ * workspace (tree_attn_plan_info) exceeds 48 MiB. Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (two streams, or a
+ * second call before the first has run) race; calls in order on one stream
+ * do not. Nothing in the array needs clearing: every partial a call reads
+ * was written by that call. */
+ta_status tree_attn_decode_noalloc(const void* q, ta_dtype q_dtype, const ta_paged_kv* kv,
+                                   const ta_plan* plan, float* out, void* hip_stream);
+
 /* Decode-loop update (plan reuse): after a decode step every leaf's new
  * tokens are appended to its KV, and the next step's queries are each leaf's
  * last queries_per_leaf tokens again. Leaf of rank r (ascending node id) grows

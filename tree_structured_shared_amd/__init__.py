@@ -192,19 +192,22 @@ class Plan:
         return bool(relaunch.value)
 
     # -- decode ---------------------------------------------------------------
-    def decode(self, q, k_pool, v_pool, out=None, stream=None):
-        """Enqueue one decode step; returns ``out`` (fp32 [n_queries, n_qheads, head_dim])."""
-        call, out = self._prepare(q, k_pool, v_pool, out, stream)
+    def decode(self, q, k_pool, v_pool, out=None, stream=None, noalloc=False):
+        """Enqueue one decode step; returns ``out`` (fp32 [n_queries, n_qheads, head_dim]).
+        noalloc: tree_attn_decode_noalloc (partials in the library's static
+        device scratch instead of the plan's workspace)."""
+        call, out = self._prepare(q, k_pool, v_pool, out, stream, noalloc)
         call()
         return out
 
-    def launcher(self, q, k_pool, v_pool, out, stream=None):
+    def launcher(self, q, k_pool, v_pool, out, stream=None, noalloc=False):
         """Check the tensors once and return a zero-argument callable that
-        enqueues tree_attn_decode with the prepared arguments (for loops that
-        decode the same buffers repeatedly)."""
-        return self._prepare(q, k_pool, v_pool, out, stream)[0]
+        enqueues tree_attn_decode (or tree_attn_decode_noalloc) with the
+        prepared arguments (for loops that decode the same buffers
+        repeatedly)."""
+        return self._prepare(q, k_pool, v_pool, out, stream, noalloc)[0]
 
-    def _prepare(self, q, k_pool, v_pool, out, stream):
+    def _prepare(self, q, k_pool, v_pool, out, stream, noalloc=False):
         import torch
         if self.host_only:
             raise TreeAttnError(1, "plan was built host_only")
@@ -235,7 +238,7 @@ class Plan:
                      stride_token=k_pool.stride(1), stride_head=k_pool.stride(2))
         if stream is None:
             stream = torch.cuda.current_stream(q.device).cuda_stream
-        fn = lib().tree_attn_decode
+        fn = lib().tree_attn_decode_noalloc if noalloc else lib().tree_attn_decode
         args = (ctypes.c_void_p(q.data_ptr()), dt, ctypes.byref(kv), self._handle,
                 ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream))
         keep = (kv, q, k_pool, v_pool, out)

@@ -24,6 +24,7 @@ EXPORTED_SYMBOLS = [
     "tree_attn_plan", "tree_attn_decode", "tree_attn_plan_info", "tree_attn_plan_export",
     "tree_attn_timing_enable", "tree_attn_timing_read", "tree_attn_plan_destroy",
     "tree_attn_last_error", "tree_attn_plan_extend", "tree_attn_kv_append", "tree_attn_plan_extend_append",
+    "tree_attn_decode_noalloc",
 ]
 
 
@@ -75,6 +76,8 @@ def lib():
     L.tree_attn_decode.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(PagedKV),
                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     L.tree_attn_decode.restype = ctypes.c_int
+    L.tree_attn_decode_noalloc.argtypes = L.tree_attn_decode.argtypes
+    L.tree_attn_decode_noalloc.restype = ctypes.c_int
     # leaf_add and new_pages are passed as addresses (int32 arrays)
     L.tree_attn_plan_extend.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                         ctypes.c_void_p, i32p]

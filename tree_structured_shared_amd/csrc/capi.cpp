@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -17,17 +18,43 @@
 #include "kernels.h"
 #include "planner.h"
 
+// The partial workspace of tree_attn_decode_noalloc: a static device array,
+// one per GPU the library runs on, held until the process ends. Host code
+// never uses its name as an address: each device's address comes from
+// hipGetSymbolAddress (scratch_of).
+constexpr size_t kScratchBytes = size_t(48) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
 
 thread_local std::string g_err;
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};  // device address of scratch on each device, once looked up
 
 ta_status set_err(ta_status s, const std::string& msg) {
   g_err = msg;
   return s;
 }
 
-ta_status hip_err(hipError_t e, const char* where) {
-  return set_err(TA_EHIP, std::string(where) + ": " + hipGetErrorString(e));
+ta_status hip_err(hipError_t e, const std::string& where) {
+  return set_err(TA_EHIP, where + ": " + hipGetErrorString(e));
+}
+
+// Device address of the static scratch on device dev (the current device),
+// looked up once per device with hipGetSymbolAddress.
+ta_status scratch_of(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return set_err(TA_EUNSUPPORTED, "static scratch: device id out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return hip_err(e, "static scratch: hipGetSymbolAddress");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return TA_OK;
 }
 
 int32_t max_slot_count(const std::vector<int32_t>& ptr) {
@@ -182,14 +209,17 @@ int64_t workspace_need(const ta_plan* p) {
   return int64_t(align256(n_pairs * p->head_dim * 4) + 2 * align256(n_pairs * 4));
 }
 
-void set_workspace_ptrs(ta_plan* p) {
+// The workspace at base: o_part, then m_part, then l_part, each 256-byte aligned.
+void workspace_layout(const ta_plan* p, void* base, float** o, float** m, float** l) {
   const size_t n_pairs = size_t(p->T.n_slots) * p->n_qheads;
   const size_t sz_o = align256(n_pairs * p->head_dim * 4), sz_m = align256(n_pairs * 4);
-  uint8_t* wb = static_cast<uint8_t*>(p->d_ws);
-  p->d_o_part = reinterpret_cast<float*>(wb);
-  p->d_m_part = reinterpret_cast<float*>(wb + sz_o);
-  p->d_l_part = reinterpret_cast<float*>(wb + sz_o + sz_m);
+  uint8_t* wb = static_cast<uint8_t*>(base);
+  *o = reinterpret_cast<float*>(wb);
+  *m = reinterpret_cast<float*>(wb + sz_o);
+  *l = reinterpret_cast<float*>(wb + sz_o + sz_m);
 }
+
+void set_workspace_ptrs(ta_plan* p) { workspace_layout(p, p->d_ws, &p->d_o_part, &p->d_m_part, &p->d_l_part); }
 
 // (Re)allocate the workspace when it no longer fits; growth keeps headroom.
 // The caller has made sure no enqueued work uses the old one.
@@ -458,6 +488,104 @@ ta_status append_args(const char* fn, const ta_paged_kv* kv, const void* k_new, 
   return TA_OK;
 }
 
+// One decode step (tree_attn_decode, tree_attn_decode_noalloc): argument
+// checks, then the partial-attention and reduction launches on hip_stream.
+// The partial results go to the plan's workspace, or, with ws_base, to the
+// same layout at ws_base (the static scratch). fn names the entry point in
+// errors.
+ta_status decode_impl(const char* fn_name, const void* q, ta_dtype q_dtype, const ta_paged_kv* kv,
+                      const ta_plan* plan, float* out, void* hip_stream, void* ws_base) {
+  const std::string fn(fn_name);
+  if (!plan) return set_err(TA_EINVAL, fn + ": plan is NULL");
+  if (plan->host_only) return set_err(TA_EINVAL, fn + ": plan was built host_only");
+  if (!plan->usable) return set_err(TA_EINVAL, fn + ": the plan is unusable after a failed update");
+  if (!q || !kv || !out || !kv->k || !kv->v)
+    return set_err(TA_EINVAL, fn + ": NULL pointer argument");
+  if (q_dtype != TA_F32 && q_dtype != TA_BF16)
+    return set_err(TA_EUNSUPPORTED, fn + ": dtype must be TA_F32 or TA_BF16");
+  if (kv->dtype != q_dtype)
+    return set_err(TA_EUNSUPPORTED, fn + ": Q and KV dtypes differ");
+  if (kv->page_size != plan->page_size)
+    return set_err(TA_EINVAL, fn + ": page_size differs from the plan's");
+  if (kv->n_pages <= int64_t(plan->T.max_page_id))
+    return set_err(TA_EINVAL, fn + ": the plan references pages beyond kv->n_pages");
+  const int64_t vec = (q_dtype == TA_BF16) ? 8 : 4;  // elements per 16 bytes
+  if (kv->stride_page <= 0 || kv->stride_token <= 0 || kv->stride_head <= 0 ||
+      kv->stride_page % vec || kv->stride_token % vec || kv->stride_head % vec)
+    return set_err(TA_EINVAL, fn + ": strides must be positive multiples of 16 bytes");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(kv->k) |
+       reinterpret_cast<uintptr_t>(kv->v) | reinterpret_cast<uintptr_t>(out)) & 15)
+    return set_err(TA_EINVAL, fn + ": pointers must be 16-byte aligned");
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_err(e, fn + ": hipGetDevice");
+  if (dev != plan->device) return set_err(TA_EINVAL, fn + ": current device differs from the plan's");
+
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  ta_plan* mp = const_cast<ta_plan*>(plan);
+  const bool timed = mp->timing_cap > 0 && mp->timing_n < mp->timing_cap;
+  if (mp->poison) {
+    e = ta::launch_fill(ws_base ? static_cast<float*>(ws_base) : mp->d_o_part, mp->ws_bytes / 4, std::nanf(""), s);
+    if (e != hipSuccess) return hip_err(e, fn + ": poison fill");
+  }
+  ta::KernelTimer t_part, t_red;
+  if (timed) {
+    hipEvent_t* ev = &mp->ev[4 * size_t(mp->timing_n)];
+    t_part = {ev[0], ev[1]};
+    t_red = {ev[2], ev[3]};
+  }
+
+  float *o_part = plan->d_o_part, *m_part = plan->d_m_part, *l_part = plan->d_l_part;
+  if (ws_base) workspace_layout(plan, ws_base, &o_part, &m_part, &l_part);
+
+  ta::PartialArgs a{};
+  a.items = plan->d_items;
+  a.group_qs = plan->d_group_qs;
+  a.group_vis = plan->d_group_vis;
+  a.seg_tok = plan->d_seg_tok;
+  a.slot_pos = plan->d_slot_pos;
+  a.q = q;
+  a.k = kv->k;
+  a.v = kv->v;
+  a.stride_page = kv->stride_page;
+  a.stride_token = kv->stride_token;
+  a.stride_head = kv->stride_head;
+  {
+    const int64_t es = (q_dtype == TA_BF16) ? 2 : 4;
+    a.sp_bytes = kv->stride_page * es;
+    a.st_bytes = kv->stride_token * es;
+    const int64_t max_off = ((kv->n_pages - 1) * kv->stride_page + (kv->page_size - 1) * kv->stride_token +
+                             int64_t(plan->n_kvheads - 1) * kv->stride_head + plan->head_dim) * es;
+    a.fast_addr = (max_off < (int64_t(1) << 32) && a.sp_bytes < (1 << 24) && a.st_bytes < (1 << 24)) ? 1 : 0;
+  }
+  a.o_part = o_part;
+  a.m_part = m_part;
+  a.l_part = l_part;
+  a.n_qheads = plan->n_qheads;
+  a.n_kvheads = plan->n_kvheads;
+  a.g = plan->g;
+  a.scale_log2 = plan->scale * 1.4426950408889634f;
+  const int dt = q_dtype == TA_BF16 ? 1 : 0;
+  const int32_t n_block = plan->T.n_items - plan->T.n_stream_items, n_wave = plan->T.n_stream_items;
+  if ((e = ta::launch_partial(a, n_block, n_wave, dt, plan->head_dim, s, t_part)) != hipSuccess)
+    return hip_err(e, fn + ": partial-attention launch");
+
+  ta::ReduceArgs r{};
+  r.q_slot_ptr = plan->d_q_slot_ptr;
+  r.o_part = o_part;
+  r.m_part = m_part;
+  r.l_part = l_part;
+  r.out = out;
+  r.n_queries = plan->T.n_queries;
+  r.n_qheads = plan->n_qheads;
+  r.max_slots = plan->max_slots;
+  e = ta::launch_reduce(r, plan->head_dim, s, t_red);
+  if (e != hipSuccess) return hip_err(e, fn + ": reduction launch");
+  if (timed) ++mp->timing_n;
+  return TA_OK;
+}
+
+
 // TREE_ATTN_LOG set (and not "0"): one line of plan statistics on stderr per
 // tree_attn_plan: groups, joined edges, chunks, items by class, partial
 // slots, the split's chunk length, workspace bytes, unique K/V tokens and the
@@ -604,90 +732,26 @@ ta_status tree_attn_plan_extend_append(ta_plan* plan, const int32_t* leaf_add, c
 ta_status tree_attn_decode(const void* q, ta_dtype q_dtype, const ta_paged_kv* kv,
                            const ta_plan* plan, float* out, void* hip_stream) {
   g_err.clear();
-  if (!plan) return set_err(TA_EINVAL, "tree_attn_decode: plan is NULL");
-  if (plan->host_only) return set_err(TA_EINVAL, "tree_attn_decode: plan was built host_only");
-  if (!plan->usable) return set_err(TA_EINVAL, "tree_attn_decode: the plan is unusable after a failed update");
-  if (!q || !kv || !out || !kv->k || !kv->v)
-    return set_err(TA_EINVAL, "tree_attn_decode: NULL pointer argument");
-  if (q_dtype != TA_F32 && q_dtype != TA_BF16)
-    return set_err(TA_EUNSUPPORTED, "tree_attn_decode: dtype must be TA_F32 or TA_BF16");
-  if (kv->dtype != q_dtype)
-    return set_err(TA_EUNSUPPORTED, "tree_attn_decode: Q and KV dtypes differ");
-  if (kv->page_size != plan->page_size)
-    return set_err(TA_EINVAL, "tree_attn_decode: page_size differs from the plan's");
-  if (kv->n_pages <= int64_t(plan->T.max_page_id))
-    return set_err(TA_EINVAL, "tree_attn_decode: the plan references pages beyond kv->n_pages");
-  const int64_t vec = (q_dtype == TA_BF16) ? 8 : 4;  // elements per 16 bytes
-  if (kv->stride_page <= 0 || kv->stride_token <= 0 || kv->stride_head <= 0 ||
-      kv->stride_page % vec || kv->stride_token % vec || kv->stride_head % vec)
-    return set_err(TA_EINVAL, "tree_attn_decode: strides must be positive multiples of 16 bytes");
-  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(kv->k) |
-       reinterpret_cast<uintptr_t>(kv->v) | reinterpret_cast<uintptr_t>(out)) & 15)
-    return set_err(TA_EINVAL, "tree_attn_decode: pointers must be 16-byte aligned");
+  return decode_impl("tree_attn_decode", q, q_dtype, kv, plan, out, hip_stream, nullptr);
+}
+
+ta_status tree_attn_decode_noalloc(const void* q, ta_dtype q_dtype, const ta_paged_kv* kv,
+                                   const ta_plan* plan, float* out, void* hip_stream) {
+  g_err.clear();
+  if (!plan) return set_err(TA_EINVAL, "tree_attn_decode_noalloc: plan is NULL");
+  if (plan->host_only) return set_err(TA_EINVAL, "tree_attn_decode_noalloc: plan was built host_only");
+  const int64_t need = workspace_need(plan);
+  if (need > int64_t(kScratchBytes))
+    return set_err(TA_EINVAL, "tree_attn_decode_noalloc: the plan's partial workspace (" + std::to_string(need) +
+                                  " bytes) exceeds the static scratch (" + std::to_string(kScratchBytes) +
+                                  " bytes)");
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_err(e, "tree_attn_decode: hipGetDevice");
-  if (dev != plan->device) return set_err(TA_EINVAL, "tree_attn_decode: current device differs from the plan's");
-
-  hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  ta_plan* mp = const_cast<ta_plan*>(plan);
-  const bool timed = mp->timing_cap > 0 && mp->timing_n < mp->timing_cap;
-  if (mp->poison) {
-    e = ta::launch_fill(mp->d_o_part, mp->ws_bytes / 4, std::nanf(""), s);
-    if (e != hipSuccess) return hip_err(e, "tree_attn_decode: poison fill");
-  }
-  ta::KernelTimer t_part, t_red;
-  if (timed) {
-    hipEvent_t* ev = &mp->ev[4 * size_t(mp->timing_n)];
-    t_part = {ev[0], ev[1]};
-    t_red = {ev[2], ev[3]};
-  }
-
-  ta::PartialArgs a{};
-  a.items = plan->d_items;
-  a.group_qs = plan->d_group_qs;
-  a.group_vis = plan->d_group_vis;
-  a.seg_tok = plan->d_seg_tok;
-  a.slot_pos = plan->d_slot_pos;
-  a.q = q;
-  a.k = kv->k;
-  a.v = kv->v;
-  a.stride_page = kv->stride_page;
-  a.stride_token = kv->stride_token;
-  a.stride_head = kv->stride_head;
-  {
-    const int64_t es = (q_dtype == TA_BF16) ? 2 : 4;
-    a.sp_bytes = kv->stride_page * es;
-    a.st_bytes = kv->stride_token * es;
-    const int64_t max_off = ((kv->n_pages - 1) * kv->stride_page + (kv->page_size - 1) * kv->stride_token +
-                             int64_t(plan->n_kvheads - 1) * kv->stride_head + plan->head_dim) * es;
-    a.fast_addr = (max_off < (int64_t(1) << 32) && a.sp_bytes < (1 << 24) && a.st_bytes < (1 << 24)) ? 1 : 0;
-  }
-  a.o_part = plan->d_o_part;
-  a.m_part = plan->d_m_part;
-  a.l_part = plan->d_l_part;
-  a.n_qheads = plan->n_qheads;
-  a.n_kvheads = plan->n_kvheads;
-  a.g = plan->g;
-  a.scale_log2 = plan->scale * 1.4426950408889634f;
-  const int dt = q_dtype == TA_BF16 ? 1 : 0;
-  const int32_t n_block = plan->T.n_items - plan->T.n_stream_items, n_wave = plan->T.n_stream_items;
-  if ((e = ta::launch_partial(a, n_block, n_wave, dt, plan->head_dim, s, t_part)) != hipSuccess)
-    return hip_err(e, "tree_attn_decode: partial-attention launch");
-
-  ta::ReduceArgs r{};
-  r.q_slot_ptr = plan->d_q_slot_ptr;
-  r.o_part = plan->d_o_part;
-  r.m_part = plan->d_m_part;
-  r.l_part = plan->d_l_part;
-  r.out = out;
-  r.n_queries = plan->T.n_queries;
-  r.n_qheads = plan->n_qheads;
-  r.max_slots = plan->max_slots;
-  e = ta::launch_reduce(r, plan->head_dim, s, t_red);
-  if (e != hipSuccess) return hip_err(e, "tree_attn_decode: reduction launch");
-  if (timed) ++mp->timing_n;
-  return TA_OK;
+  if (e != hipSuccess) return hip_err(e, "tree_attn_decode_noalloc: hipGetDevice");
+  void* ws = nullptr;
+  const ta_status st = scratch_of(dev, &ws);
+  if (st != TA_OK) return st;
+  return decode_impl("tree_attn_decode_noalloc", q, q_dtype, kv, plan, out, hip_stream, ws);
 }
 
 ta_status tree_attn_kv_append(const ta_paged_kv* kv, const void* k_new, const void* v_new, int64_t n_tokens,
