@@ -82,6 +82,8 @@ typedef struct {
                                 (device plans) 4 the device tables, 5 the workspace; each
                                 tree_attn_plan_extend adds one host step first, then its
                                 device steps (staging, regrown tables and workspace) */
+  int32_t force_staging;     /* testing: in-place table updates of tree_attn_plan_extend always go
+                                through the pinned staging buffer, never the kernel arguments */
 } ta_plan_opts;
 
 /* Paged K/V pools on the device. Element strides; head_dim is contiguous.
@@ -266,7 +268,12 @@ enum {
                              the words after it, up to the next group's offset (at least 96),
                              repeat tokens of the same segment (the kernels read ahead) */
   TA_T_GROUP_SEG = 15,    /* [n_groups] offset of each group's segment in TA_T_SEG_TOK */
-  TA_T_COUNT = 16
+  TA_T_UPDATE_COUNTS = 16,/* [3] device-table updates so far: in-place in the kernel arguments,
+                             in-place through the pinned staging buffer, whole uploads */
+  TA_T_DEVICE_TABLES = 17,/* the device copy of the kernels' tables (work items, group queries,
+                             visible prefixes, page table, slot tables), read back from the
+                             device; the call waits for the device. TA_EINVAL if host_only */
+  TA_T_COUNT = 18
 };
 
 #ifdef __cplusplus

@@ -65,7 +65,10 @@ static ta_status plan_tree(const tree* t, ta_plan_opts* o, ta_plan** p) {
 }
 
 static void export_all(const ta_plan* p) {
+  int64_t none = 0;  /* host-only plans have no device tables to read back */
+  CHECK(tree_attn_plan_export(p, TA_T_DEVICE_TABLES, NULL, &none) == TA_EINVAL, "device tables of a host-only plan");
   for (int32_t id = 0; id < TA_T_COUNT; ++id) {
+    if (id == TA_T_DEVICE_TABLES) continue;
     int64_t len = 0;
     CHECK(tree_attn_plan_export(p, id, NULL, &len) == TA_OK, "export len %d", id);
     int32_t* buf = (int32_t*)malloc(sizeof(int32_t) * (size_t)(len ? len : 1));

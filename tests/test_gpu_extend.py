@@ -269,3 +269,61 @@ def test_fused_append_extend_matches_separate_calls(dtype, d):
         inst = grown
     for p in plans:
         p.close()
+
+
+def test_update_routes_write_identical_device_tables():
+    """In-place table updates travel in the kernel arguments when they fit
+    (at most 448 words) and through the pinned staging buffer otherwise.
+    Twin plans, one forced onto the staging route, grow over steps whose
+    updates fall under and over that size: their device tables (read back
+    from the device) and decode outputs are identical every step, and the
+    update counts show which route each step took."""
+    n_leaf = 20
+    inst = synth.make_tree([-1] + [0] * n_leaf, [400] + [20 + 3 * i for i in range(n_leaf)], page_size=16, qpl=1,
+                           n_qheads=8, n_kvheads=2, head_dim=128, dtype=torch.bfloat16, seed=9)
+    inst = synth.fill_tensors(inst, seed=10)
+    spare = n_leaf * 8 * 4
+    k = torch.zeros((inst.n_pages + spare,) + tuple(inst.k_pool.shape[1:]), dtype=inst.dtype, device="cuda")
+    v = torch.full(k.shape, synth.CANARY_V, dtype=torch.float32, device="cuda").to(inst.dtype)
+    k[:inst.n_pages].copy_(inst.k_pool)
+    v[:inst.n_pages].copy_(inst.v_pool)
+    plans = [Plan.for_instance(inst), Plan.for_instance(inst, force_staging=True)]
+    seen_args = seen_staging = False
+    # step 0 uploads whole; then one leaf gains a token (a small update: its
+    # item, its visible length, one page-table word), then every leaf gains
+    # 100 (a large one: 2,000 page-table words), alternating
+    for step in range(6):
+        add = np.zeros(inst.n_leaves, np.int64)
+        if step == 0:
+            add[:] = 1
+        elif step % 2 == 1:
+            add[step % inst.n_leaves] = 1
+        else:
+            add[:] = 100
+        grown, new_pages = synth.grow_leaves(inst, add, seed=800 + step)
+        assert grown.n_pages <= k.shape[0]
+        k[inst.n_pages:grown.n_pages].copy_(grown.k_pool[inst.n_pages:])
+        v[inst.n_pages:grown.n_pages].copy_(grown.v_pool[inst.n_pages:])
+        for (pg, grown_pg) in ((k, grown.k_pool), (v, grown.v_pool)):
+            pg[:grown.n_pages].copy_(grown_pg)
+        before = [p.export("update_counts").copy() for p in plans]
+        rel = [p.extend(add, new_pages) for p in plans]
+        assert rel[0] == rel[1]
+        after = [p.export("update_counts") for p in plans]
+        d = [a - b for a, b in zip(after, before)]
+        _log(f"route step {step}: default {d[0].tolist()} forced staging {d[1].tolist()}")
+        assert d[1][0] == 0                      # the forced plan never uses the arguments
+        if d[0][2] == 0:                         # an in-place step on both
+            assert d[0].sum() == 1 and d[1].sum() == 1 and d[1][1] == 1
+            seen_args |= bool(d[0][0])
+            seen_staging |= bool(d[0][1])
+        dt = [p.export("device_tables") for p in plans]
+        assert dt[0].shape == dt[1].shape and np.array_equal(dt[0], dt[1]), f"step {step}: device tables differ"
+        outs = [p.decode(grown.q.cuda(), k, v) for p in plans]
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0], outs[1]), f"step {step}: outputs differ"
+        _check(outs[0], ta.decode_instance(grown), f"update routes step {step}")
+        inst = grown
+    assert seen_args and seen_staging, (seen_args, seen_staging)
+    for p in plans:
+        p.close()

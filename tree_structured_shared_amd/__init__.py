@@ -98,7 +98,7 @@ class Plan:
                  queries_per_leaf, n_qheads, n_kvheads, head_dim, *, force_edges=None,
                  host_only=False, scale=0.0, poison_workspace=False, ts_q=0, ts_c=0, gamma=0,
                  rb=0, waves=0, floor_f=0, ncu=0, split=True, stream_rows=0, split_align=0,
-                 tile_join=True, fail_alloc_after=0):
+                 tile_join=True, fail_alloc_after=0, force_staging=False):
         L = lib()
         self._handle = ctypes.c_void_p()
         par, par_p = _i32(parent)
@@ -113,7 +113,8 @@ class Plan:
                         ncu=ncu, no_split=0 if split else 1, host_only=1 if host_only else 0,
                         scale=float(scale), poison_workspace=1 if poison_workspace else 0,
                         stream_rows=int(stream_rows), split_align=int(split_align),
-                        no_tile_join=0 if tile_join else 1, fail_alloc_after=int(fail_alloc_after))
+                        no_tile_join=0 if tile_join else 1, fail_alloc_after=int(fail_alloc_after),
+                        force_staging=1 if force_staging else 0)
         self._force = None
         if force_edges is not None:
             fe = np.ascontiguousarray(np.asarray(force_edges), dtype=np.int8)
@@ -157,7 +158,9 @@ class Plan:
         return out.reshape(-1, cols) if cols else out
 
     def tables(self):
-        return {k: self.export(k) for k in TABLE_IDS}
+        """The planner's tables (not the library's update counts or the
+        device read-back)."""
+        return {k: self.export(k) for k in TABLE_IDS if k not in ("update_counts", "device_tables")}
 
     # -- decode loop ----------------------------------------------------------
     def extend(self, leaf_add, new_pages=(), stream=None, append=None):

@@ -16,7 +16,7 @@ STATUS_NAMES = {0: "TA_OK", 1: "TA_EINVAL", 2: "TA_ENOMEM", 3: "TA_EHIP", 4: "TA
 TABLE_IDS = {
     "params": 0, "edges": 1, "nq": 2, "lcum": 3, "groups": 4, "group_qs": 5, "group_vis": 6,
     "chunks": 7, "items": 8, "q_slot_ptr": 9, "q_slots": 10, "runs": 11, "chunk_run_ptr": 12,
-    "bfs": 13, "seg_tok": 14, "group_seg": 15,
+    "bfs": 13, "seg_tok": 14, "group_seg": 15, "update_counts": 16, "device_tables": 17,
 }
 TABLE_COLS = {"groups": 8, "chunks": 3, "items": 5, "runs": 3}
 
@@ -37,7 +37,7 @@ class PlanOpts(ctypes.Structure):
         ("scale", ctypes.c_float), ("poison_workspace", ctypes.c_int32),
         ("stream_rows", ctypes.c_int32),
         ("split_align", ctypes.c_int32), ("no_tile_join", ctypes.c_int32),
-        ("fail_alloc_after", ctypes.c_int32),
+        ("fail_alloc_after", ctypes.c_int32), ("force_staging", ctypes.c_int32),
     ]
 
 

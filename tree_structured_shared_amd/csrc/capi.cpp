@@ -104,6 +104,13 @@ struct ta_plan {
   // testing (ta_plan_opts.fail_alloc_after): the plan's fail_after-th
   // allocation step fails as if out of memory; alloc_steps counts the steps
   int32_t fail_after = 0, alloc_steps = 0;
+  // testing (ta_plan_opts.force_staging): in-place table updates always go
+  // through the pinned staging buffer, never the kernel arguments
+  int32_t force_staging = 0;
+  // how each device-table update went: in the kernel arguments, through the
+  // pinned staging buffer, or as a whole upload (TA_T_UPDATE_COUNTS)
+  std::vector<int32_t> update_counts = std::vector<int32_t>(3, 0);
+  std::vector<int32_t> device_copy;  // TA_T_DEVICE_TABLES, read back on export
 };
 
 namespace {
@@ -131,6 +138,8 @@ const std::vector<int32_t>* table_ptr(const ta_plan* p, int32_t id) {
     case TA_T_BFS: return &T.bfs;
     case TA_T_SEG_TOK: return &T.seg_tok;
     case TA_T_GROUP_SEG: return &T.group_seg_base;
+    case TA_T_UPDATE_COUNTS: return &p->update_counts;
+    case TA_T_DEVICE_TABLES: return &p->device_copy;
     default: return nullptr;
   }
 }
@@ -344,7 +353,7 @@ ta_status upload_incremental(ta_plan* p, hipStream_t s, const ta::AppendArgs* ap
   const size_t words = desc.size() + data.size();
   if (words >= size_t(INT32_MAX)) return set_err(TA_EINVAL, "tree_attn_plan_extend: update too large");
   hipError_t e;
-  if (words <= size_t(ta::kArgStageWords)) {
+  if (words <= size_t(ta::kArgStageWords) && !p->force_staging) {
     // small update: descriptors and words travel in the kernel arguments
     ta::ArgStage st{};
     std::memcpy(st.w, desc.data(), desc.size() * 4);
@@ -353,6 +362,7 @@ ta_status upload_incremental(ta_plan* p, hipStream_t s, const ta::AppendArgs* ap
                                     s)) != hipSuccess)
       return hip_err(e, "tree_attn_plan_extend: table update launch");
     *app_done = app != nullptr;
+    ++p->update_counts[0];
     return TA_OK;
   }
   // pinned host staging, read by the scatter kernel in place: this buffer's
@@ -387,6 +397,7 @@ ta_status upload_incremental(ta_plan* p, hipStream_t s, const ta::AppendArgs* ap
     return hip_err(e, "tree_attn_plan_extend: hipEventRecord");
   p->stage_used[b] = true;
   p->stage_next = b ^ 1;
+  ++p->update_counts[1];
   return TA_OK;
 }
 
@@ -432,6 +443,7 @@ ta_status extend_impl(ta_plan* plan, const int32_t* leaf_add, const int32_t* new
       if (e != hipSuccess) return hip_err(e, "tree_attn_plan_extend: hipDeviceSynchronize");
       st = upload_full(plan, true, &moved);
       plan->sized_for_growth = true;
+      if (st == TA_OK) ++plan->update_counts[2];
     }
     if (st != TA_OK) {
       plan->usable = false;
@@ -625,7 +637,7 @@ ta_status tree_attn_plan(const int32_t* parent, int32_t n_nodes, const int32_t* 
   ta_plan* p = nullptr;
   try {
     ta::PlanParams pp;
-    int32_t host_only = 0, poison = 0;
+    int32_t host_only = 0, poison = 0, force_staging = 0;
     float scale = 0.0f;
     if (opts) {
       if (opts->ts_q) pp.ts_q = opts->ts_q;
@@ -644,6 +656,7 @@ ta_status tree_attn_plan(const int32_t* parent, int32_t n_nodes, const int32_t* 
       if (opts->split_align) pp.split_align = opts->split_align;
       pp.tile_join = opts->no_tile_join ? 0 : 1;
       if (opts->fail_alloc_after < 0) return set_err(TA_EINVAL, "tree_attn_plan: negative fail_alloc_after");
+      force_staging = opts->force_staging ? 1 : 0;
     }
     const int32_t fail_after = opts ? opts->fail_alloc_after : 0;
     if (fail_after == 1) return set_err(TA_ENOMEM, "tree_attn_plan: host allocation failed (plan)");
@@ -661,6 +674,7 @@ ta_status tree_attn_plan(const int32_t* parent, int32_t n_nodes, const int32_t* 
     if (!(scale >= 0.0f) || std::isinf(scale)) return set_err(TA_EINVAL, "tree_attn_plan: bad scale");
     p = new ta_plan;
     p->fail_after = fail_after;
+    p->force_staging = force_staging;
     p->alloc_steps = 1;  // the plan object
     std::string err;
     if (alloc_fails(p)) throw std::bad_alloc();  // testing: the planner state
@@ -785,6 +799,19 @@ ta_status tree_attn_plan_info(const ta_plan* plan, int32_t* n_queries, int64_t* 
 ta_status tree_attn_plan_export(const ta_plan* plan, int32_t table_id, int32_t* dst, int64_t* len) {
   g_err.clear();
   if (!plan || !len) return set_err(TA_EINVAL, "tree_attn_plan_export: NULL plan or len");
+  if (table_id == TA_T_DEVICE_TABLES) {  // the device copy, read back (waits for the device)
+    if (plan->host_only) return set_err(TA_EINVAL, "tree_attn_plan_export: host_only plans have no device tables");
+    try {
+      ta_plan* mp = const_cast<ta_plan*>(plan);
+      mp->device_copy.resize(plan->tables_words);
+      hipError_t e = hipDeviceSynchronize();
+      if (e == hipSuccess)
+        e = hipMemcpy(mp->device_copy.data(), plan->d_tables, plan->tables_words * 4, hipMemcpyDeviceToHost);
+      if (e != hipSuccess) return hip_err(e, "tree_attn_plan_export: device tables");
+    } catch (const std::bad_alloc&) {
+      return set_err(TA_ENOMEM, "tree_attn_plan_export: host allocation failed");
+    }
+  }
   const std::vector<int32_t>* t = table_ptr(plan, table_id);
   if (!t) return set_err(TA_EINVAL, "tree_attn_plan_export: unknown table id");
   if (dst) {

@@ -1282,8 +1282,10 @@ __global__ void update_kernel(AppendArgs a, int32_t* dst, int64_t dst_words, con
 
 // The same with the staged words in the kernel arguments (read in place from
 // the argument segment). The whole argument list stays within 4 KiB.
+// (explicit arguments, each 8-byte aligned at most, plus up to 256 bytes of
+// the hidden arguments code-object v5 appends)
 static_assert(sizeof(AppendArgs) + sizeof(int32_t*) + sizeof(int64_t) + sizeof(ArgStage) + 2 * sizeof(int32_t) +
-                      64 <= 4096,
+                      6 * 8 + 256 <= 4096,
               "update_args_kernel's arguments fit a 4 KiB argument block");
 __global__ void update_args_kernel(AppendArgs a, int32_t* dst, int64_t dst_words, ArgStage st, int32_t n_desc,
                                    int32_t sb) {
