@@ -432,6 +432,10 @@ struct MfmaState {
   f32x4 O[NRTW][DPL];
   f32x4 L4[NRTW];  // l by MFMA (ones x P^T): every element of lane (i, j) is row i's l
   float m[NRTW], l[NRTW];
+  // split threshold per row: log2 units, m + log2(kLoFrac l) as of the last
+  // exact decision (-inf before the first); a tile whose row max stays at or
+  // below it cannot hold a weight above kLoFrac of the running sum
+  float thr[NRTW];
   RowRef row[NRTW];
   int vmin[NRTW];  // wave-uniform: smallest visible length over the tile's valid rows
   bool on[NRTW];   // wave-uniform: row tile k exists
@@ -451,6 +455,7 @@ __device__ __forceinline__ void mfma_init(MfmaState<D, NRTW>& S, const PartialAr
     S.row[k] = row_ref(a, it, h, on[k] ? rt[k] * 16 + i : it.nrows);
     S.m[k] = kMInit;
     S.l[k] = 0.0f;
+    S.thr[k] = TA_NEG_INF;
     S.L4[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int db = 0; db < DPL; ++db) S.O[k][db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -515,8 +520,8 @@ __device__ __forceinline__ void load_tile_kv(TileKV<D>& b, const TileSeg& sg, co
 // mfma_softmax_max: masks tokens at or past the row's limit (the score
 // accumulators s0, s1 are rewritten in place; skipped, wave-uniformly, when
 // the whole tile is visible to every row of the tile), raises the running
-// max when needed (rescaling l and O) and returns the row's largest weight
-// of the tile, exp2(tile max - running max).
+// max when needed (rescaling l and O) and returns the row's max of the tile
+// (scaled, log2 units).
 //
 // mfma_softmax_weights<SPLIT>: the weights as MFMA B operands, each rounded
 // once to bf16 (pb) or, SPLIT, as a bf16 pair pb + pl (~16 bits of P);
@@ -533,7 +538,8 @@ __device__ __forceinline__ void load_tile_kv(TileKV<D>& b, const TileSeg& sg, co
 // whenever some row's largest weight of the tile exceeds kLoFrac of that
 // row's running sum l including the tile (split_needed): the sums only grow
 // (in the scale of the current max), so every weight left single-rounded is
-// at most kLoFrac of L. The decision is a ballot over the wave.
+// at most kLoFrac of L. The decision is a ballot over the wave, exact only
+// when a row's max passes a cached threshold (split_needed).
 template <int D, int NRTW>
 __device__ __forceinline__ float mfma_softmax_max(MfmaState<D, NRTW>& S, int k, f32x4& s0, f32x4& s1,
                                                   const PartialArgs& a, const WorkItem& it, int base, int j) {
@@ -565,13 +571,24 @@ __device__ __forceinline__ float mfma_softmax_max(MfmaState<D, NRTW>& S, int k, 
     for (int db = 0; db < DPL; ++db) S.O[k][db] *= al;
     S.m[k] = raise ? mx : S.m[k];
   }
-  return fast_exp2(mx - S.m[k]);
+  return mx;
 }
 
-// wave-uniform: some row's largest weight of the tile is above kLoFrac of
-// its running sum l (this tile included)
-__device__ __forceinline__ bool split_needed(float pmax, float l) {
-  return __builtin_amdgcn_ballot_w64(pmax > kLoFrac * l) != 0;
+// The split decision of a row tile (wave-uniform), given each row's tile
+// max mx (scaled) and its running sum l including the tile. The exact test
+// (some row's largest weight exp2(mx - m) above kLoFrac l) costs an exp2, a
+// compare and, in workgroup waves, a wait for the row-sum MFMA; it runs only
+// when some row's mx exceeds its cached threshold thr = m + log2(kLoFrac l)
+// (from the last exact test). Sums only grow and a rescale moves m and
+// log2 l by the same amount, so a row at or below its threshold needs no
+// split. The exact test refreshes the thresholds. l is passed as a function
+// so the caller's sum is only formed when needed.
+template <int D, int NRTW, typename LF>
+__device__ __forceinline__ bool split_needed(MfmaState<D, NRTW>& S, int k, float mx, LF lsum) {
+  if (!__builtin_amdgcn_ballot_w64(mx > S.thr[k])) return false;
+  const float l = lsum();
+  S.thr[k] = S.m[k] + __builtin_amdgcn_logf(kLoFrac * l);
+  return __builtin_amdgcn_ballot_w64(fast_exp2(mx - S.m[k]) > kLoFrac * l) != 0;
 }
 
 template <int D, int NRTW, bool SPLIT, bool LMF = false>
@@ -626,10 +643,10 @@ __device__ __forceinline__ void mfma_tile(MfmaState<D, NRTW>& S, const TileKV<D>
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b.k[1][kk]), S.qf[k][kk], s1, 0, 0, 0);
     }
     bf16x8 pb, pl;
-    const float pmax = mfma_softmax_max<D, NRTW>(S, k, s0, s1, a, it, base, j);
+    const float mx = mfma_softmax_max<D, NRTW>(S, k, s0, s1, a, it, base, j);
     const float l0 = S.l[k];
     mfma_softmax_weights<D, NRTW, false>(S, k, s0, s1, a, pb, pl);
-    if (split_needed(pmax, sum4rows(S.l[k]))) {  // the weights again, split; l takes them unrounded
+    if (split_needed(S, k, mx, [&] { return sum4rows(S.l[k]); })) {  // again, split; l takes them unrounded
       S.l[k] = l0;
       mfma_softmax_weights<D, NRTW, true>(S, k, s0, s1, a, pb, pl);
 #pragma unroll
@@ -908,11 +925,11 @@ __device__ __forceinline__ void lds_tile(MfmaState<D, NRTW>& S, const char* stag
   bf16x8 pb[NACT];
 #pragma unroll
   for (int k = 0; k < NACT; ++k) {
-    const float pmax = mfma_softmax_max<D, NRTW>(S, k, s0[k], s1[k], a, it, base, j);
+    const float mx = mfma_softmax_max<D, NRTW>(S, k, s0[k], s1[k], a, it, base, j);
     bf16x8 pl;
     mfma_softmax_weights<D, NRTW, false, true>(S, k, s0[k], s1[k], a, pb[k], pl);
     S.L4[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[k], S.L4[k], 0, 0, 0);
-    if (split_needed(pmax, S.L4[k][0])) {  // the weights again, split (pb as before)
+    if (split_needed(S, k, mx, [&] { return S.L4[k][0]; })) {  // the weights again, split (pb as before)
       mfma_softmax_weights<D, NRTW, true, true>(S, k, s0[k], s1[k], a, pb[k], pl);
       S.L4[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pl, S.L4[k], 0, 0, 0);
 #pragma unroll
