@@ -14,8 +14,9 @@
 // leaves, large ones near the root):
 //  * workgroup items (many rows): one workgroup per item x kv-head. bf16:
 //    the workgroup streams each K/V tile once into LDS with direct loads
-//    (kLdsStages stages, one barrier per tile) and wave w computes row tiles
-//    w and w+4 (128 rows per workgroup) from it. fp32: each wave runs the
+//    (kLdsStages stages, one barrier per tile); up to 64 rows, wave w
+//    computes 16-row tile w from it, above that (up to 128 rows) one 32-row
+//    tile each on the 32x32 matrix instruction. fp32: each wave runs the
 //    GEMV path on row pairs.
 //  * single-wave items (up to 16 rows): each wave is one item x kv-head and
 //    streams its chunk alone with two tiles in flight.
@@ -63,7 +64,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBlock = 256;
 constexpr int kWaves = 4;
-constexpr int kBlockRowTiles = 2; // 16-row tiles per wave in workgroup items
+constexpr int kBlockRowTiles = 2; // rows per wave in a workgroup pass, in 16-row tiles
 constexpr float kRescale = 8.0f;  // lazy-rescale threshold, log2 units
 // a row tile's weights enter P V as a bf16 hi + lo pair when some row's
 // largest weight of the tile exceeds this share of its running sum
@@ -945,6 +946,191 @@ __device__ __forceinline__ void lds_tile(MfmaState<D, NRTW>& S, const char* stag
   }
 }
 
+// Workgroup waves of wide row blocks (more than 64 rows): one 32-row tile
+// per wave on v_mfma_f32_32x32x16_bf16, so every K and V operand read from
+// LDS feeds 32 rows and the per-tile softmax bookkeeping (max, rescale and
+// split tests, addresses) is shared by 32 rows instead of 16. Same transposed
+// formulation as the 16-row tiles: S^T = K Q^T and O^T = V^T P^T. Operand
+// layouts (lane l, h = l / 32): A[i = l % 32][k = 8h + e], B[k = 8h + e][j =
+// l % 32], D[i = 8 (v / 4) + 4h + v % 4][j = l % 32] for e < 8, v < 16. So
+// lane l holds 16 of the 32 scores of row l % 32 (tokens 8 (v / 4) + 4h +
+// v % 4), and the other 16 sit in lane l ^ 32. P V k-step s (tokens 16 s ..
+// 16 s + 15) takes the lane's scores v = 8 s .. 8 s + 7 as its B operand as
+// they stand; the V^T operand uses the same token order, tokens 16 s + 4h +
+// [0, 4) and 16 s + 8 + 4h + [0, 4), read from LDS by two transpose reads.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <int D>
+struct WideState {
+  static constexpr int KS = D / 16, DB = D / 32;
+  bf16x8 qf[KS];  // Q^T: row l % 32, d = 16 kk + 8h + [0, 8)
+  f32x16 O[DB];   // O^T: d = 32 db + 8 (v / 4) + 4h + v % 4, row l % 32
+  f32x16 L;       // ones x P^T: every element is row l % 32's l
+  float m, thr;   // running max and split threshold (as in MfmaState)
+  RowRef row;
+  int vmin;       // wave-uniform: smallest visible length over the tile's rows
+};
+
+// rows rbeg + [0, 32) of the item (those below it.nrows)
+template <int D>
+__device__ __forceinline__ void wide_init(WideState<D>& W, const PartialArgs& a, const WorkItem& it, int h,
+                                          int rbeg) {
+  constexpr int KS = D / 16, DB = D / 32;
+  const int lane = threadIdx.x & 63;
+  W.row = row_ref(a, it, h, rbeg + (lane & 31));
+  W.m = kMInit;
+  W.thr = TA_NEG_INF;
+  W.L = f32x16{};
+#pragma unroll
+  for (int db = 0; db < DB; ++db) W.O[db] = f32x16{};
+  {
+    float v = W.row.ok ? float(W.row.vis) : 3.0e38f;
+#pragma unroll
+    for (int x = 1; x < 32; x <<= 1) v = fminf(v, __shfl_xor(v, x, 64));
+    W.vmin = __builtin_amdgcn_readfirstlane(int(fminf(v, 2.0e9f)));
+  }
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+    for (int x = 0; x < 8; ++x) W.qf[kk][x] = __bf16(0.0f);
+  if (W.row.ok) {
+    const __bf16* qp = reinterpret_cast<const __bf16*>(a.q) + (int64_t(W.row.gq) * a.n_qheads + W.row.qh) * D +
+                       8 * (lane >> 5);
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) W.qf[kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
+  }
+}
+
+// One 32-token tile of a 32-row tile, operands from an LDS stage (LdsTile
+// layout: K chunk c of token t at c ^ t, V chunk c at c ^ 2t, both mod 16 at
+// D = 128; the K reads of 8 consecutive tokens and the transpose reads of 4
+// tokens x 2 chunks then fall on distinct banks).
+template <int D>
+__device__ __forceinline__ void wide_tile(WideState<D>& W, const char* stage, const PartialArgs& a,
+                                          const WorkItem& it, int base) {
+  typedef LdsTile<D> L;
+  constexpr int KS = D / 16, DB = D / 32;
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 5, t32 = lane & 31;
+  f32x16 sc = f32x16{};
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(stage + L::off(0, t32, 2 * kk + h));
+    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, W.qf[kk], sc, 0, 0, 0);
+  }
+  const float c = a.scale_log2;
+  if (base + 32 > min(it.tok1, W.vmin)) {  // wave-uniform: some token of the tile is masked
+    const int lim = min(it.tok1, W.row.vis) - base - 4 * h;
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      if (8 * (v >> 2) + (v & 3) >= lim) sc[v] = TA_NEG_INF;
+  }
+  // row max over the lane's 16 scores (three-input maxes, which take the
+  // matrix-core results without quieting them first), then over lane l ^ 32
+  float mx = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
+  mx = fmaxf(fmaxf(mx, sc[3]), sc[4]);
+  mx = fmaxf(fmaxf(mx, sc[5]), sc[6]);
+  mx = fmaxf(fmaxf(mx, sc[7]), sc[8]);
+  mx = fmaxf(fmaxf(mx, sc[9]), sc[10]);
+  mx = fmaxf(fmaxf(mx, sc[11]), sc[12]);
+  mx = fmaxf(fmaxf(mx, sc[13]), sc[14]);
+  mx = fmaxf(fmaxf(mx, sc[15]), sc[0]);
+  {
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mx = fmaxf(fmaxf(mx, __uint_as_float(b[0])), __uint_as_float(b[1])) * c;
+  }
+  const bool raise = mx > W.m + kRescale;
+  if (__builtin_amdgcn_ballot_w64(raise)) {  // rare after the first tiles
+    const float al = raise ? fast_exp2(W.m - mx) : 1.0f;
+    W.L *= al;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) W.O[db] *= al;
+    W.m = raise ? mx : W.m;
+  }
+  // V^T operand of k-step ks and d block db: lane (16 G + x) of group G
+  // points at token 16 ks + 8 half + 4 (G / 2) + x / 4, d = 32 db + 16 (G % 2)
+  // + 4 (x % 4); a transpose read hands lane l the values at d = 32 db + l % 32
+  // of tokens 16 ks + 8 half + 4h + [0, 4). The swizzle depends on the token
+  // mod 8 only, so ks and half are immediate offsets.
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4s lds_v4s;
+  typedef __attribute__((address_space(3))) char lds_b;
+  const lds_b* vstage = (const lds_b*)stage + L::PART;
+  const int G = lane >> 4, x = lane & 15;
+  const int tv = 4 * (G >> 1) + (x >> 2);
+  auto vt_of = [&](int ks, int db) {
+    v4s part[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int t = 16 * ks + 8 * half + tv;
+      const int ch = 4 * db + 2 * (G & 1) + ((x & 3) >> 1);
+      part[half] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4s*)(vstage + t * L::ROW + ((ch ^ L::swz(1, t)) << 4) + 8 * (x & 1)));
+    }
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  const bf16x8 ones = {__bf16(1.0f), __bf16(1.0f), __bf16(1.0f), __bf16(1.0f),
+                       __bf16(1.0f), __bf16(1.0f), __bf16(1.0f), __bf16(1.0f)};
+  const float nm = -W.m;
+  bf16x8 pb[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pb[ks][e] = __bf16(fast_exp2(__builtin_fmaf(sc[8 * ks + e], c, nm)));
+    W.L = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[ks], W.L, 0, 0, 0);
+  }
+  // the split decision (as split_needed: an exact test only when some row's
+  // max passes its cached threshold); a split tile adds its lo halves to O
+  // and l at once
+  if (__builtin_amdgcn_ballot_w64(mx > W.thr)) {
+    const float l = W.L[0];
+    W.thr = W.m + __builtin_amdgcn_logf(kLoFrac * l);
+    if (__builtin_amdgcn_ballot_w64(fast_exp2(mx - W.m) > kLoFrac * l)) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 pl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = fast_exp2(__builtin_fmaf(sc[8 * ks + e], c, nm));
+          pl[e] = __bf16(p - float(pb[ks][e]));
+        }
+        W.L = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pl, W.L, 0, 0, 0);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          W.O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt_of(ks, db), pl, W.O[db], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      W.O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt_of(ks, db), pb[ks], W.O[db], 0, 0, 0);
+}
+
+// lane l writes the d values it holds of row l % 32: runs of 4 at
+// 32 db + 8 u + 4h (u < 4); lanes of the first half write m and l
+template <int D>
+__device__ __forceinline__ void wide_write(const WideState<D>& W, const PartialArgs& a) {
+  constexpr int DB = D / 32;
+  const int h = (threadIdx.x & 63) >> 5;
+  if (!W.row.ok) return;
+  int32_t pi32 = W.row.pi;
+  asm volatile("" : "+v"(pi32));
+  const int64_t pi = pi32;
+  float* op = a.o_part + pi * D + 4 * h;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      *reinterpret_cast<f32x4*>(op + 32 * db + 8 * u) =
+          f32x4{W.O[db][4 * u], W.O[db][4 * u + 1], W.O[db][4 * u + 2], W.O[db][4 * u + 3]};
+  if (h == 0) {
+    a.m_part[pi] = W.m;
+    a.l_part[pi] = W.L[0];
+  }
+}
+
 // The tile loop of a workgroup item: kLdsStages LDS stages filled by direct
 // loads kLdsStages - 1 tiles ahead. Per tile: wait for this wave's own
 // loads of the tile (explicit vmcnt: the direct loads are invisible to the
@@ -958,6 +1144,16 @@ __device__ __forceinline__ void lds_tile(MfmaState<D, NRTW>& S, const char* stag
 // page-table read is clamped to the chunk's last token (loads past the last
 // tile fetch written K/V that the softmax never uses). NACT (row tiles this
 // wave computes) is fixed per loop.
+
+// The tile loop's body over its NS stages: stage S takes tile n + S (while
+// there is one), with S a compile-time constant.
+template <int S, int NS, typename F>
+__device__ __forceinline__ void unroll_stages(int n, int ntiles, F& f) {
+  if constexpr (S < NS) {
+    if (S == 0 || n + S < ntiles) f(n + S, std::integral_constant<int, S>());
+    unroll_stages<S + 1, NS>(n, ntiles, f);
+  }
+}
 
 // s_waitcnt with vmcnt = n (< 16) and no wait on the other counters
 template <int N>
@@ -977,9 +1173,10 @@ __device__ __forceinline__ void lds_stage_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-template <int D, bool FA, int NACT>
-__device__ __forceinline__ void lds_stream(MfmaState<D, kBlockRowTiles>& S, char* lds, const PartialArgs& a,
-                                           const WorkItem& it, int h, int i, int j) {
+// body(stage, base): the compute of one tile (base = its first token), or
+// nothing for a wave without rows
+template <int D, bool FA, typename Body>
+__device__ __forceinline__ void lds_stream(char* lds, const PartialArgs& a, const WorkItem& it, int h, Body body) {
   typedef TileDma<D, FA> Dma;
   typedef LdsTile<D> L;
   typedef __attribute__((address_space(3))) char lds_char;
@@ -1047,16 +1244,10 @@ __device__ __forceinline__ void lds_stream(MfmaState<D, kBlockRowTiles>& S, char
     constexpr int SF = SG == 0 ? NS - 1 : SG - 1;  // the stage of tile n - 1, done by every wave
     dma.issue(lds + SF * ST, w, a);
     dma4(st, word_off(n + 2 * AHEAD), lds_addr(SF * ST + wpos));
-    if constexpr (NACT > 0)
-      lds_tile<D, kBlockRowTiles, NACT>(S, lds + SG * ST, a, it, it.tok0 + n * 32, i, j);
+    body(lds + SG * ST, it.tok0 + n * 32);
   };
-  static_assert(NS == 3, "the loop is unrolled over three stages");
-  // wave-uniform: tile n sits in stage n mod 3
-  for (int n = 0; n < ntiles; n += NS) {
-    step(n, std::integral_constant<int, 0>());
-    if (n + 1 < ntiles) step(n + 1, std::integral_constant<int, 1>());
-    if (n + 2 < ntiles) step(n + 2, std::integral_constant<int, 2>());
-  }
+  // wave-uniform: tile n sits in stage n mod NS
+  for (int n = 0; n < ntiles; n += NS) unroll_stages<0, NS>(n, ntiles, step);
   // every wave's direct loads (the clamped ones past the end included) land
   // before the stages are reused
   lds_stage_barrier<0>();
@@ -1074,21 +1265,31 @@ __device__ __forceinline__ void block_lds_item(const PartialArgs& a, char* lds, 
   // row tiles beyond kWaves * kBlockRowTiles take further passes over the
   // chunk (the planner's row blocks keep this to one pass)
   for (int r0 = 0; r0 < nrt; r0 += kWaves * kBlockRowTiles) {
-    int rt[kBlockRowTiles];
-    bool on[kBlockRowTiles];
-#pragma unroll
-    for (int k = 0; k < kBlockRowTiles; ++k) {
-      rt[k] = r0 + wave + kWaves * k;
-      on[k] = rt[k] < nrt;
-    }
-    MfmaState<D, kBlockRowTiles> S;
-    mfma_init(S, a, it, h, rt, on);
     // every wave takes part in the loads and barriers, computing or not
-    if (S.on[1]) lds_stream<D, FA, 2>(S, lds, a, it, h, i, j);
-    else if (S.on[0]) lds_stream<D, FA, 1>(S, lds, a, it, h, i, j);
-    else lds_stream<D, FA, 0>(S, lds, a, it, h, i, j);
+    auto idle = [](const char*, int) {};
+    if (nrt - r0 > kWaves) {
+      // more than 64 rows in this pass: wave w computes rows 32 w .. 32 w + 31
+      // of the pass as one 32-row tile
+      WideState<D> W;
+      wide_init(W, a, it, h, (r0 + 2 * wave) * 16);
+      if (2 * wave < nrt - r0)
+        lds_stream<D, FA>(lds, a, it, h, [&](const char* st, int base) { wide_tile<D>(W, st, a, it, base); });
+      else
+        lds_stream<D, FA>(lds, a, it, h, idle);
+      wide_write(W, a);
+      continue;
+    }
+    // at most 64 rows: wave w computes 16-row tile w of the pass
+    const int rt[1] = {r0 + wave};
+    const bool on[1] = {r0 + wave < nrt};
+    MfmaState<D, 1> S;
+    mfma_init(S, a, it, h, rt, on);
+    if (S.on[0])
+      lds_stream<D, FA>(lds, a, it, h, [&](const char* st, int base) { lds_tile<D, 1, 1>(S, st, a, it, base, i, j); });
+    else
+      lds_stream<D, FA>(lds, a, it, h, idle);
     // V^T came from transpose reads (d = 16 db + 4j + c), l from the matrix cores
-    mfma_write<D, kBlockRowTiles, true>(S, a);
+    mfma_write<D, 1, true>(S, a);
   }
 }
 
