@@ -33,8 +33,8 @@ ROOT_LEN = 1100  # every query sees more than 1024 tokens
 def peaky_tree(cls, kind, dtype, d, seed=0):
     """cls 'wave': every group has at most 16 rows (single-wave items only).
     cls 'workgroup': a 192-row root and 16-row leaves (leaf-local causal
-    mask, qpl 4): workgroup items only, waves with two and with one row
-    tile."""
+    mask, qpl 4): workgroup items only; the root's 96-row blocks run 32-row
+    tiles (32x32 matrix instruction), the leaves 16-row tiles."""
     if cls == "wave":
         par, lens, qpl = [-1, 0, 0, 0, 0], [ROOT_LEN, 60, 200, 350, 33], 1
     else:
