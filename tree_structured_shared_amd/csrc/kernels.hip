@@ -78,9 +78,6 @@ constexpr float kMInit = -1.0e30f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
 // Byte offset of a pool token from its page-table entry (page << 8 | slot).
 // FA: every offset fits 32 bits and both byte strides fit 24 bits, so two
 // full-rate 24-bit multiplies do it and loads take the uniform-base +
@@ -184,12 +181,15 @@ __device__ __forceinline__ const char* pool_head(const void* pool, const Partial
 }
 
 // ---------------------------------------------------------------------------
-// GEMV path: up to R rows. A wave streams tokens with 8 lanes per token (each
-// lane owns D/8 consecutive head-dim elements) and 2 tokens per 8-lane group
-// per step; every 8-lane group keeps its own online-softmax state, merged
-// across the wave at the end.
+// GEMV path (fp32 inputs): up to R rows. A wave streams tokens with 8 lanes
+// per token (each lane owns D/8 consecutive head-dim elements) and 2 tokens
+// per 8-lane group per step; every 8-lane group keeps its own online-softmax
+// state, merged across the wave at the end. bf16 items of one or two rows
+// run the 16-row matrix tile instead: it keeps twice the bytes in flight,
+// and this loop on bf16 measured slower on the multi-level prompt.
 template <typename T, int EPL>
 struct Slice {  // EPL elements of one token row, as 16-byte words
+  static_assert(std::is_same<T, float>::value, "the GEMV path reads fp32 rows");
   static constexpr int kWords = EPL * int(sizeof(T)) / 16;
   u32x4 w[kWords];
   template <typename O>
@@ -198,20 +198,10 @@ struct Slice {  // EPL elements of one token row, as 16-byte words
     for (int c = 0; c < kWords; ++c) w[c] = load_at<u32x4>(base, off + O(16 * c));
   }
   __device__ __forceinline__ void to_float(float* out) const {
-    if constexpr (std::is_same<T, float>::value) {
 #pragma unroll
-      for (int c = 0; c < kWords; ++c)
+    for (int c = 0; c < kWords; ++c)
 #pragma unroll
-        for (int x = 0; x < 4; ++x) out[4 * c + x] = __uint_as_float(w[c][x]);
-    } else {
-#pragma unroll
-      for (int c = 0; c < kWords; ++c)
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          out[8 * c + 2 * x] = bf_lo(w[c][x]);
-          out[8 * c + 2 * x + 1] = bf_hi(w[c][x]);
-        }
-    }
+      for (int x = 0; x < 4; ++x) out[4 * c + x] = __uint_as_float(w[c][x]);
   }
 };
 
