@@ -58,7 +58,7 @@ typedef enum { TA_F32 = 0, TA_BF16 = 1 } ta_dtype;
 typedef struct {
   int32_t ts_q;    /* query tile of the padding cost (default 16) */
   int32_t ts_c;    /* context tile of the padding cost (default 64) */
-  int32_t gamma;   /* intermediate-result cost per query, in token units (default 32) */
+  int32_t gamma;   /* intermediate-result cost per query, in token units (default 128 x n_qheads / n_kvheads) */
   int32_t rb;      /* maximum rows (query x q-head-in-group) per work item (default 128) */
   int32_t waves;   /* target busy waves per CU for the split rule (default 5) */
   int32_t floor_f; /* chunk length floor, in tokens per row (default 4) */

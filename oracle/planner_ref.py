@@ -24,7 +24,11 @@ with the reasons in the design notes):
 * SplitKVCost = C_P(nQ_curr, len_v) + C_P(nQ_l, len_l) + gamma * nQ_l;
   SplitQCost  = C_P(nQ_curr - nQ_l, len_v) + C_P(nQ_l, len_l + len_v);
   C_P = C_{P,q} + C_{P,c}; the common factor d is dropped; Pad(TS, 0) = 0.
-* Constants (not printed on the page): TS_q = 16, TS_c = 64, gamma = 32.
+* Constants (not printed on the page): TS_q = 16, TS_c = 64, and gamma =
+  128 g per query, g = n_qheads / n_kvheads: nQ counts query tokens, a query's
+  partials are g rows of d fp32 values written and read back (8 g d bytes per
+  kv-head) against d / 4 bytes per query-token of K/V shared by a 16-query
+  tile (32 g in these units), times four as measured on the target GPU.
 * Split rule, row blocks, work-item classes and order, slot numbering and
   page runs are this library's own, written out step by step below. Groups
   with at most ``stream_rows`` rows become single-wave stream items (one row
@@ -56,7 +60,7 @@ T_PARAMS, T_EDGES, T_NQ, T_LCUM, T_GROUPS, T_GROUP_QS, T_GROUP_VIS, T_CHUNKS, T_
 TABLE_NAMES = ["params", "edges", "nq", "lcum", "groups", "group_qs", "group_vis", "chunks",
                "items", "q_slot_ptr", "q_slots", "runs", "chunk_run_ptr", "bfs"]
 
-DEFAULTS = dict(ts_q=16, ts_c=64, gamma=32, rb=128, waves=5, floor_f=4, ncu=256, split=1,
+DEFAULTS = dict(ts_q=16, ts_c=64, gamma=0, rb=128, waves=5, floor_f=4, ncu=256, split=1,
                 stream_rows=16, split_align=128, tile_join=1)
 
 
@@ -112,6 +116,8 @@ def build_plan(parent, node_len, node_page_ptr, node_page_ids, page_size, qpl,
     if "tile_join" in opts:
         o["tile_join"] = int(opts["tile_join"])
     o["stream_rows"] = max(0, o["stream_rows"])     # negative: no single-wave items
+    if o["gamma"] == 0:   # the default: 128 per q-head of a kv-head's group
+        o["gamma"] = min(2**31 - 1, 128 * (n_qheads // max(1, n_kvheads)))
     ts_q, ts_c, gamma, rb = o["ts_q"], o["ts_c"], o["gamma"], o["rb"]
     parent = [int(x) for x in parent]
     lens = [int(x) for x in node_len]
@@ -276,21 +282,33 @@ def build_plan(parent, node_len, node_page_ptr, node_page_ids, page_size, qpl,
                 t0 += nt
         G["nblocks"] = len(G["blocks"])
         G["rb"] = max(nr for _, nr in G["blocks"])
+    def chunking(G, c_glob):
+        """(chunk length, chunk count) of group G under global chunk c_glob:
+        at least the group's floor, then balanced pieces, 16-aligned."""
+        kvl = G["kv_len"]
+        cg = max(c_glob, _align_up(o["floor_f"] * min(G["rows"], G["rb"]), o["split_align"]))
+        nch = _cdiv(kvl, cg)
+        csz = _align_up(_cdiv(kvl, nch), CHUNK_ALIGN)
+        return csz, _cdiv(kvl, csz)
+
     if o["split"]:
         W = H * sum((3 if G["cls"] == 0 else BLOCK_WAVE_WEIGHT3) * G["nblocks"] * G["kv_len"]
                     for G in groups)
         U = _cdiv(W, o["ncu"] * o["waves"] * 3)
         c_glob = max(o["split_align"], _align_up(U, o["split_align"]))
+        # the launch fills the GPU (review 3.3): while it would hold fewer
+        # units (item x kv-head) than compute units, the global chunk steps
+        # down by one alignment
+        while c_glob > o["split_align"] and \
+                H * sum(G["nblocks"] * chunking(G, c_glob)[1] for G in groups) < o["ncu"]:
+            c_glob -= o["split_align"]
     else:
         c_glob = 0
     chunks = []
     for gi, G in enumerate(groups):
         kvl = G["kv_len"]
         if o["split"]:
-            cg = max(c_glob, _align_up(o["floor_f"] * min(G["rows"], G["rb"]), o["split_align"]))
-            nch = _cdiv(kvl, cg)
-            csz = _align_up(_cdiv(kvl, nch), CHUNK_ALIGN)
-            nch = _cdiv(kvl, csz)
+            csz, nch = chunking(G, c_glob)
         else:
             csz, nch = kvl, 1
         G["chunk_ptr"] = len(chunks)

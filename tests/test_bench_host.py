@@ -37,7 +37,8 @@ def test_streamed_bytes_count_each_row_block_once_per_chunk():
     # blocks, each streaming the root; each leaf group (128 rows) streams its own tokens once
     inst = synth.make_tree([-1, 0, 0], [300, 40, 50], page_size=16, qpl=2, n_qheads=64, n_kvheads=1,
                            head_dim=128, seed=3)
-    plan = Plan.for_instance(inst, host_only=True, split=False)
+    # (a small intermediate-result cost keeps both edges split at this GQA)
+    plan = Plan.for_instance(inst, host_only=True, split=False, gamma=32)
     assert not plan.export("edges").any()
     assert b.streamed_kv_bytes(plan, inst) == (2 * 300 + 40 + 50) * 1 * 128 * 2 * 2
     plan.close()

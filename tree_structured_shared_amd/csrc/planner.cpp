@@ -8,7 +8,8 @@
 //  P4  greedy binary edge assignment -- FastTree review, section 3.2,
 //      Algorithm 1: for each child l of v (BFS order) compare the cost of
 //      keeping the edge split (SplitKVCost: padding of both groups plus the
-//      intermediate result gamma * nQ_l) with joining it (SplitQCost: v keeps
+//      intermediate result gamma * nQ_l, gamma = 128 g by default) with
+//      joining it (SplitQCost: v keeps
 //      nQ_curr - nQ_l queries, l reads len_l + len_v); assign 1 iff C0 >= C1.
 //      Padding cost C_P(n, len) = Pad(TS_q, n) * len + n * Pad(TS_c, min(len, TS_c))
 //      with Pad(TS, N) = TS - ((N - 1) % TS + 1) (section 3.2 cost model; the
@@ -24,9 +25,10 @@
 //  P7  long-context split (FastTree review, section 3.3): a global chunk
 //      length sized so the launch gives about ncu * waves busy waves (a
 //      workgroup block counts as kBlockWaveWeight3 / 3 waves: its four waves
-//      share each staged tile), a multiple of split_align, floored per group
-//      at floor_f tokens per row; each group's chunks are then balanced and
-//      16-aligned.
+//      share each staged tile), a multiple of split_align, stepped down while
+//      the launch would hold fewer units than compute units, floored per
+//      group at floor_f tokens per row; each group's chunks are then balanced
+//      and 16-aligned.
 //  P8  work items: workgroup items first, then stream items, each class
 //      longest first (stable).
 //  P9  partial-result slots: group, then chunk, then query.
@@ -121,6 +123,8 @@ int plan_init(const int32_t* parent, int32_t n, const int32_t* node_len,
   PlanState S;
   S.p = p;
   S.p.force_edges = nullptr;
+  if (S.p.gamma == 0)
+    S.p.gamma = int32_t(std::min<int64_t>(INT32_MAX, int64_t(kGammaPerGroupHead) * (n_qheads / n_kvheads)));
   S.n = n;
   S.root = root;
   S.qpl = qpl;
@@ -205,7 +209,7 @@ int plan_init(const int32_t* parent, int32_t n, const int32_t* node_len,
         assign = p.force_edges[l] ? 1 : 0;
       } else {
         const int64_t c0 = pad_cost(nq_curr, len_v, p.ts_q, p.ts_c) +
-                           pad_cost(nq_l, len_l, p.ts_q, p.ts_c) + int64_t(p.gamma) * nq_l;
+                           pad_cost(nq_l, len_l, p.ts_q, p.ts_c) + int64_t(S.p.gamma) * nq_l;
         const int64_t c1 = pad_cost(nq_curr - nq_l, len_v, p.ts_q, p.ts_c) +
                            pad_cost(nq_l, len_l + len_v, p.ts_q, p.ts_c);
         assign = (c0 >= c1) ? 1 : 0;
@@ -320,6 +324,15 @@ void plan_layout(PlanState& S, PlanTables& T) {
   }
 
   // ---- P7 chunks
+  // a group's chunk length and count under global chunk cg_glob: at least the
+  // group's floor, then balanced pieces, 16-aligned
+  auto chunking = [&](const PlanGroup& G, int64_t cg_glob, int64_t* csz, int64_t* nch) {
+    const int64_t cg =
+        std::max<int64_t>(cg_glob, align_up(int64_t(p.floor_f) * std::min(G.rows, G.rb), p.split_align));
+    *nch = cdiv(G.kv_len, cg);
+    *csz = align_up(cdiv(G.kv_len, *nch), kChunkAlign);
+    *nch = cdiv(G.kv_len, *csz);
+  };
   int64_t c_glob = 0;
   if (p.split) {
     int64_t W = 0;
@@ -327,17 +340,25 @@ void plan_layout(PlanState& S, PlanTables& T) {
     W *= H;
     const int64_t U = cdiv(W, int64_t(p.ncu) * p.waves * 3);
     c_glob = std::max<int64_t>(p.split_align, align_up(U, p.split_align));
+    // the launch fills the GPU (review 3.3): while it would hold fewer units
+    // (item x kv-head) than compute units, the global chunk steps down by one
+    // alignment
+    auto units = [&](int64_t cg_glob) {
+      int64_t u = 0, csz, nch;
+      for (const PlanGroup& G : S.groups) {
+        chunking(G, cg_glob, &csz, &nch);
+        u += int64_t(G.nblocks) * nch;
+      }
+      return u * H;
+    };
+    while (c_glob > p.split_align && units(c_glob) < p.ncu) c_glob -= p.split_align;
   }
   T.chunks.clear();
   for (int32_t gi = 0; gi < int32_t(S.groups.size()); ++gi) {
     PlanGroup& G = S.groups[gi];
     int64_t csz, nch;
     if (p.split) {
-      const int64_t cg =
-          std::max<int64_t>(c_glob, align_up(int64_t(p.floor_f) * std::min(G.rows, G.rb), p.split_align));
-      nch = cdiv(G.kv_len, cg);
-      csz = align_up(cdiv(G.kv_len, nch), kChunkAlign);
-      nch = cdiv(G.kv_len, csz);
+      chunking(G, c_glob, &csz, &nch);
     } else {
       csz = G.kv_len;
       nch = 1;

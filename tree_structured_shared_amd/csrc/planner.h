@@ -9,7 +9,8 @@
 namespace ta {
 
 struct PlanParams {
-  int32_t ts_q = 16, ts_c = 64, gamma = 32, rb = 128, waves = 5, floor_f = 4, ncu = 256;
+  // gamma 0: kGammaPerGroupHead * (n_qheads / n_kvheads), resolved by plan_init
+  int32_t ts_q = 16, ts_c = 64, gamma = 0, rb = 128, waves = 5, floor_f = 4, ncu = 256;
   int32_t split_align = 128;  // chunk lengths of the split are multiples of this
   int32_t split = 1;
   int32_t stream_rows = 16;  // groups with at most this many rows run as one-wave items
@@ -18,6 +19,13 @@ struct PlanParams {
 };
 
 constexpr int32_t kFormatVersion = 4;
+// Default intermediate-result cost per query (greedy edge assignment), in the
+// cost model's query-token units, per q-head of a kv-head's group: a query's
+// partials are g rows of d fp32 values written and read back (8 g d bytes per
+// kv-head) against d / 4 bytes per query-token of K/V streamed once for a
+// 16-query tile, i.e. 32 g; measured on MI355X, a partial costs about four
+// times its bytes (the reduction's second pass and its launch), so 128 g.
+constexpr int32_t kGammaPerGroupHead = 128;
 constexpr int32_t kTileRows = 16;       // rows of one MFMA row tile
 constexpr int64_t kBlockWaveWeight3 = 8; // split rule: a workgroup block counts as 8/3 busy waves
 constexpr int32_t kChunkAlign = 16;     // chunk lengths are multiples of the MFMA token block
