@@ -66,6 +66,28 @@ def test_workload_costs_by_hand():
     assert pr.split_q_cost(10, 1, 400, 32000, 16, 64) == 710000
 
 
+def test_default_intermediate_cost_scales_with_the_gqa_group():
+    """The default gamma is 128 per q-head of a kv-head's group (nQ counts query
+    tokens; each query leaves g partial rows per kv-head). Root of 256 tokens,
+    two 64-token leaves with 2 query tokens each:
+      first child:  C0 = CP(4, 256) + CP(2, 64) + 2 gamma = 3072 + 896 + 2 gamma
+                    C1 = CP(2, 256) + CP(2, 320) = 3584 + 4480 = 8064
+      g = 4  (gamma 512):  C0 = 4992 < 8064 -> 0, and the same for the second child;
+      g = 16 (gamma 2048): C0 = 8064 >= 8064 -> 1 (the printed tie rule); then
+      second child with cur = 2: C0 = 3584 + 896 + 4096 = 8576 >= CP(0, 256) +
+      CP(2, 320) = 4480 -> 1, and the root keeps no queries."""
+    lens = np.array([256, 64, 64], np.int32)
+    ptr = np.concatenate([[0], np.cumsum((lens + 15) // 16)]).astype(np.int32)
+    ids = np.arange(ptr[-1], dtype=np.int32)
+    for hq, hk, edges, root_q, gamma in [(16, 4, [0, 0], 4, 512), (64, 4, [1, 1], 0, 2048)]:
+        plan = pr.build_plan([-1, 0, 0], lens, ptr, ids, 16, 2, hq, hk, 128)
+        assert plan["params"][10] == gamma
+        assert plan["edges"][1:].tolist() == edges
+        assert plan["nq"][0] == root_q
+    assert pr.cost_pad(4, 256, 16, 64) == 3072 and pr.cost_pad(2, 64, 16, 64) == 896
+    assert pr.cost_pad(2, 256, 16, 64) == 3584 and pr.cost_pad(2, 320, 16, 64) == 4480
+
+
 @pytest.mark.parametrize("k", [1, 2, 3, 4])
 def test_simple_trees_aggregate_directly(k):
     """Simple trees keep every edge at 0 (the review's ablation: the greedy
