@@ -7,7 +7,12 @@
 // (section 3, kernel design: every group dispatched to its own blocks of one
 // launch) -- with a flash-style online softmax over 32-token tiles (DeFT
 // notes, attention calculation; FastTree review, tile-by-tile online softmax).
-// Each row ends in one unnormalised partial (m, l, o) in the workspace.
+// Each row ends in one partial (m, l, o) in the workspace: o unnormalised in
+// fp32, or, when every |o / l| of the row is below 1, o / l as fp16 in the
+// first half of the row's record with l stored negated (the reduction reads
+// the sign). The fp16 form rounds each value by at most 2^-12, a convex
+// combination of them moves the output by no more, and it halves the
+// partial results written and read back.
 //
 // One launch (partial_kernel) holds both item classes, chosen per group by
 // its row count (the review's multi-stage query tiling: small tiles near the
@@ -61,6 +66,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kBlock = 256;
 constexpr int kWaves = 4;
@@ -700,11 +707,63 @@ __device__ __forceinline__ void mfma_write(MfmaState<D, NRTW>& S, const PartialA
   for (int k = 0; k < NRTW; ++k) {
     if (!S.on[k]) continue;
     const float l = LM ? S.L4[k][0] : sum4rows(S.l[k]);
+    // the row's largest |o| over its four lanes, before any lane leaves
+    float mx = 0.0f;
+#pragma unroll
+    for (int db = 0; db < DPL; ++db)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) mx = fmaxf(mx, fabsf(S.O[k][db][c]));
+    mx = max4rows(mx);
+    const bool half = mx < l;  // every |o / l| below 1
     if (!S.row[k].ok) continue;
     int32_t pi32 = S.row[k].pi;
     asm volatile("" : "+v"(pi32));  // keep the 32-bit index live over the loop, widen here
     const int64_t pi = pi32;
-    if constexpr (TR) {
+    if (half) {
+      const float inv = 1.0f / l;
+      if constexpr (TR) {
+        // lane j holds the 4-runs d = 16 db + 4 j; lanes j and j ^ 1 (l ^ 16)
+        // trade one run per pair of d blocks over permlane16, so even j
+        // stores d = 16 db + 4 j + [0, 8) of the even block and odd j d = 16 db
+        // + 4 (j - 1) + [0, 8) of the odd one, each as one 16-byte store (the
+        // row's four lanes take the same half path)
+        const bool odd = j & 1;
+        _Float16* hp = reinterpret_cast<_Float16*>(a.o_part + pi * D) + 4 * (j & ~1);
+#pragma unroll
+        for (int q = 0; q < DPL / 2; ++q) {
+          u32x2 run[2];  // blocks 2 q, 2 q + 1
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const f32x4& o4 = S.O[k][2 * q + e];
+            const f16x4 hv4 = {_Float16(o4[0] * inv), _Float16(o4[1] * inv), _Float16(o4[2] * inv),
+                               _Float16(o4[3] * inv)};
+            run[e] = __builtin_bit_cast(u32x2, hv4);
+          }
+          const u32x2 send = odd ? run[0] : run[1];
+          u32x2 got;
+#pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            const auto r = __builtin_amdgcn_permlane16_swap(send[w], send[w], false, false);
+            got[w] = (threadIdx.x & 16) ? r[0] : r[1];
+          }
+          const u32x4 out = odd ? u32x4{got[0], got[1], run[1][0], run[1][1]}
+                                : u32x4{run[0][0], run[0][1], got[0], got[1]};
+          *reinterpret_cast<u32x4*>(hp + 16 * (2 * q + (odd ? 1 : 0))) = out;
+        }
+      } else {
+        _Float16* hp = reinterpret_cast<_Float16*>(a.o_part + pi * D) + 4 * j * DPL;
+#pragma unroll
+        for (int x8 = 0; x8 < DPL / 2; ++x8) {
+          f16x8 v;
+#pragma unroll
+          for (int y = 0; y < 8; ++y) {
+            const int x = 8 * x8 + y;  // local offset = c * DPL + db
+            v[y] = _Float16(S.O[k][x % DPL][x / DPL] * inv);
+          }
+          *reinterpret_cast<f16x8*>(hp + 8 * x8) = v;
+        }
+      }
+    } else if constexpr (TR) {
       float* op = a.o_part + pi * D + 4 * j;
 #pragma unroll
       for (int db = 0; db < DPL; ++db) *reinterpret_cast<f32x4*>(op + 16 * db) = S.O[k][db];
@@ -723,7 +782,7 @@ __device__ __forceinline__ void mfma_write(MfmaState<D, NRTW>& S, const PartialA
     }
     if (j == 0) {
       a.m_part[pi] = S.m[k];
-      a.l_part[pi] = l;
+      a.l_part[pi] = half ? -l : l;
     }
   }
 }
@@ -1104,20 +1163,65 @@ template <int D>
 __device__ __forceinline__ void wide_write(const WideState<D>& W, const PartialArgs& a) {
   constexpr int DB = D / 32;
   const int h = (threadIdx.x & 63) >> 5;
+  // the row's largest |o| (lanes l and l ^ 32 hold its two halves), before
+  // any lane leaves
+  const float l = W.L[0];
+  float mx = 0.0f;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, fabsf(W.O[db][v]));
+  mx = fmaxf(mx, xor32(mx));
+  const bool half = mx < l;  // every |o / l| below 1
   if (!W.row.ok) return;
   int32_t pi32 = W.row.pi;
   asm volatile("" : "+v"(pi32));
   const int64_t pi = pi32;
-  float* op = a.o_part + pi * D + 4 * h;
+  if (half) {
+    // lane h holds the 4-runs d = 32 db + 8 u + 4 h; for each pair of runs u
+    // = 2 p, 2 p + 1 the lanes trade one run over permlane32, so lane h = 0
+    // stores d = 32 db + 16 p + [0, 8) and lane h = 1 the next 8, each as one
+    // 16-byte store (a row's two lanes take the same half path: one l, one mx)
+    const float inv = 1.0f / l;
+    _Float16* hp = reinterpret_cast<_Float16*>(a.o_part + pi * D) + 8 * h;
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      *reinterpret_cast<f32x4*>(op + 32 * db + 8 * u) =
-          f32x4{W.O[db][4 * u], W.O[db][4 * u + 1], W.O[db][4 * u + 2], W.O[db][4 * u + 3]};
+      for (int pp = 0; pp < 2; ++pp) {
+        u32x2 run[2];  // runs u = 2 pp, 2 pp + 1 as packed halves
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int u = 2 * pp + q;
+          const f16x4 hv4 = {_Float16(W.O[db][4 * u] * inv), _Float16(W.O[db][4 * u + 1] * inv),
+                             _Float16(W.O[db][4 * u + 2] * inv), _Float16(W.O[db][4 * u + 3] * inv)};
+          run[q] = __builtin_bit_cast(u32x2, hv4);
+        }
+        // h = 0 keeps run 0 and sends run 1; h = 1 keeps run 1 and sends run 0
+        const u32x2 send = h ? run[0] : run[1];
+        u32x2 got;
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          const auto r = __builtin_amdgcn_permlane32_swap(send[w], send[w], false, false);
+          got[w] = h ? r[0] : r[1];
+        }
+        // h = 0: own d 8u..8u+3 of u = 2pp then the partner's 8u+4..8u+7;
+        // h = 1: the partner's d 8u..8u+3 of u = 2pp+1 then its own 8u+4..8u+7
+        const u32x4 out = h ? u32x4{got[0], got[1], run[1][0], run[1][1]}
+                            : u32x4{run[0][0], run[0][1], got[0], got[1]};
+        *reinterpret_cast<u32x4*>(hp + 32 * db + 16 * pp) = out;
+      }
+  } else {
+    float* op = a.o_part + pi * D + 4 * h;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        *reinterpret_cast<f32x4*>(op + 32 * db + 8 * u) =
+            f32x4{W.O[db][4 * u], W.O[db][4 * u + 1], W.O[db][4 * u + 2], W.O[db][4 * u + 3]};
+  }
   if (h == 0) {
     a.m_part[pi] = W.m;
-    a.l_part[pi] = W.L[0];
+    a.l_part[pi] = half ? -l : l;
   }
 }
 
@@ -1356,6 +1460,7 @@ __global__ __launch_bounds__(kBlock) void lse_reduce_kernel(ReduceArgs a) {
   constexpr int kReduceBatch = B;
   constexpr int EPL = D / 16;         // output elements per lane
   constexpr int GP = kReduceGroups / P;  // lane groups per pair
+  typedef _Float16 hv_t __attribute__((ext_vector_type(EPL)));
   const int64_t n_pairs = int64_t(a.n_queries) * a.n_qheads;
   const int64_t wave_id = int64_t(blockIdx.x) * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wave_id * P >= n_pairs) return;
@@ -1381,16 +1486,23 @@ __global__ __launch_bounds__(kBlock) void lse_reduce_kernel(ReduceArgs a) {
 #pragma unroll
     for (int u = 0; u < kReduceBatch; ++u)
       pi[u] = int64_t(s0) * a.n_qheads + int64_t(hq) * (s1 - s0) + (min(b + GP * u, s1 - 1) - s0);
+    // every slot's fp16 half-record is requested with its m and l; the slots
+    // kept in fp32 (l not negated) are then read whole
     float mv[kReduceBatch], lv[kReduceBatch];
+    hv_t hv[kReduceBatch];
     f32x4 ov[kReduceBatch][EPL / 4];
 #pragma unroll
     for (int u = 0; u < kReduceBatch; ++u) {
       mv[u] = (b + GP * u < s1) ? a.m_part[pi[u]] : TA_NEG_INF;
       lv[u] = a.l_part[pi[u]];
-#pragma unroll
-      for (int c = 0; c < EPL / 4; ++c)
-        ov[u][c] = *reinterpret_cast<const f32x4*>(a.o_part + pi[u] * D + sub * EPL + 4 * c);
+      hv[u] = *reinterpret_cast<const hv_t*>(reinterpret_cast<const _Float16*>(a.o_part + pi[u] * D) + sub * EPL);
     }
+#pragma unroll
+    for (int u = 0; u < kReduceBatch; ++u)
+      if (!__builtin_signbit(lv[u]))
+#pragma unroll
+        for (int c = 0; c < EPL / 4; ++c)
+          ov[u][c] = *reinterpret_cast<const f32x4*>(a.o_part + pi[u] * D + sub * EPL + 4 * c);
     float Mn = M;
 #pragma unroll
     for (int u = 0; u < kReduceBatch; ++u) Mn = fmaxf(Mn, mv[u]);
@@ -1401,11 +1513,14 @@ __global__ __launch_bounds__(kBlock) void lse_reduce_kernel(ReduceArgs a) {
 #pragma unroll
     for (int u = 0; u < kReduceBatch; ++u) {
       const float w = part_weight(mv[u], Mn);
-      L += lv[u] * w;
+      const bool half = __builtin_signbit(lv[u]);
+      const float lu = fabsf(lv[u]);
+      L += lu * w;
+      const float sc = half ? lu * w : w;  // fp16 records hold o / l
 #pragma unroll
       for (int c = 0; c < EPL / 4; ++c)
 #pragma unroll
-        for (int y = 0; y < 4; ++y) acc[4 * c + y] += ov[u][c][y] * w;
+        for (int y = 0; y < 4; ++y) acc[4 * c + y] += (half ? float(hv[u][4 * c + y]) : ov[u][c][y]) * sc;
     }
     M = Mn;
   }
