@@ -90,3 +90,44 @@ def test_flat_inputs_do_not_reach_the_rescale():
     inst = peaky_tree("workgroup", "none", torch.bfloat16, 128)
     rise, _ = _rise_and_spread(inst)
     assert rise < RESCALE_LOG2, rise
+
+
+def _record_forms(inst):
+    """(rows whose partial o / l stays inside (-1, 1), rows with a value of
+    magnitude 1 or more): the two workspace forms the kernels choose between
+    (fp16 o / l, fp32 o), from fp64 chunk softmaxes of the instance's own rows."""
+    q = inst.q.to(torch.float64).numpy()
+    g = inst.n_qheads // inst.n_kvheads
+    c = 1.0 / np.sqrt(inst.head_dim)
+    half = full = 0
+    for toks, ch, qs, vis in _segments(inst):
+        nodes = sorted({u for u, _ in toks})
+        kv = {u: (ta.node_kv(inst.k_pool, u, inst.node_len, inst.node_page_ptr, inst.node_page_ids, inst.page_size),
+                  ta.node_kv(inst.v_pool, u, inst.node_len, inst.node_page_ptr, inst.node_page_ids, inst.page_size))
+              for u in nodes}
+        K = np.stack([kv[u][0][t] for u, t in toks])
+        V = np.stack([kv[u][1][t] for u, t in toks])
+        for qi, nv in zip(qs, vis):
+            for h in range(inst.n_qheads):
+                s = K[:nv, h // g] @ q[qi, h] * c
+                for a, b in ch:
+                    b = min(b, nv)
+                    if a >= b:
+                        continue
+                    w = np.exp(s[a:b] - s[a:b].max())
+                    o = (w @ V[a:b, h // g]) / w.sum()
+                    if np.abs(o).max() < 1.0:
+                        half += 1
+                    else:
+                        full += 1
+    return half, full
+
+
+def test_both_partial_record_forms_occur():
+    """N(0,1) inputs give partials that are weighted averages well inside
+    (-1, 1) (fp16 records); a dominant key carries its own value, whose
+    largest component exceeds 1 (fp32 records)."""
+    half, full = _record_forms(peaky_tree("workgroup", "none", torch.bfloat16, 128))
+    assert half > 0 and full <= 0.01 * (half + full), (half, full)
+    half, full = _record_forms(peaky_tree("workgroup", "sink", torch.bfloat16, 128))
+    assert half > 0 and full > 0, (half, full)
