@@ -43,18 +43,19 @@ struct PartialArgs {
   int64_t sp_bytes, st_bytes;   // page and token strides in bytes
   int32_t fast_addr;            // 1: every pool byte offset fits 32 bits and both
                                 // byte strides fit 24 bits (24-bit multiplies)
-  float* o_part;   // [n_slots (by position), n_qheads, D] unnormalised
+  float* o_part;   // [n_slots (by position), n_qheads, D] records: o unnormalised in fp32, or
+                   // (every |o| below l) o / l as D fp16 values in the record's first half
   float* m_part;   // [n_slots (by position), n_qheads] running max, base-2 scaled units
-  float* l_part;   // [n_slots (by position), n_qheads] sum of exp2(s - m)
+  float* l_part;   // [n_slots (by position), n_qheads] sum of exp2(s - m), negated for fp16 records
   int32_t n_qheads, n_kvheads, g;
   float scale_log2;  // softmax scale * log2(e)
 };
 
 struct ReduceArgs {
   const int32_t* q_slot_ptr;  // query q holds slots [q_slot_ptr[q], q_slot_ptr[q + 1]) (pair-major workspace)
-  const float* o_part;
+  const float* o_part;  // records as the partial kernel writes them (fp32 o, or fp16 o / l)
   const float* m_part;
-  const float* l_part;
+  const float* l_part;  // negative (or -0) for an fp16 record
   float* out;  // [n_q, n_qheads, D]
   int32_t n_queries, n_qheads;
   int32_t max_slots;  // largest slot count of one query (sets the pairs per wave)
