@@ -809,14 +809,19 @@ __device__ __forceinline__ void mfma_wave(const PartialArgs& a, const WorkItem& 
 // direct-to-LDS loads into one of kLdsStages stages (two tiles in flight while
 // one is computed), and one barrier per tile hands a stage over. Token rows
 // are stored with their 16-byte chunks XOR-swizzled by the token index, so the
-// MFMA operand reads hit distinct banks. K rows are read 16 tokens x one
-// chunk at a time: chunk c of token t sits at c ^ t. V rows are read by
-// transpose reads, 8 tokens x 2 adjacent chunks per half wave: at 16 chunks
-// a row (D = 128) chunk c of token t sits at c ^ 2t, which maps those 16
-// pieces to 16 distinct 16-byte positions of a row (c ^ t would put token t,
-// chunk 2b and token t ^ 1, chunk 2b + 1 on the same banks); at 8 chunks a
-// row two tokens share a 256-byte bank line and c ^ t already spreads them.
-// A stage ends in each wave's page-table words for the tile two later.
+// MFMA operand reads hit distinct banks (a half wave's 32 lanes read one
+// 256-byte bank line per cycle). K rows are read 16 tokens x one chunk at a
+// time: chunk c of token t sits at c ^ t. V rows are read by transpose reads,
+// whose half waves take 8 tokens x 2 adjacent chunks (16-row tiles) or
+// 4 tokens x 4 adjacent chunks (32-row tiles, chunks 4k .. 4k + 3). At 16
+// chunks a row (D = 128) chunk c of token t sits at c ^ sv(t), sv(t) =
+// 4 (t mod 4) + 2 (bit 2 of t): over 8 aligned tokens sv takes the 8 even
+// values, and over 4 aligned tokens its bits 2 and 3 take all four values,
+// so either read puts its 16 pieces of a half wave on 16 distinct 16-byte
+// positions (c ^ 2t would leave the 4-token reads two-way conflicted);
+// at 8 chunks a row two tokens share a 256-byte bank line and c ^ t already
+// spreads them. A stage ends in each wave's page-table words for the tile two
+// later.
 template <int D>
 struct LdsTile {
   static constexpr int CH = D / 8;         // 16-byte chunks per token row
@@ -826,7 +831,8 @@ struct LdsTile {
   static constexpr int STAGE = 2 * PART + kWaves * WORDS;  // K, V, then the words
   // XOR applied to the chunk index of token t's row in part 0 (K) or 1 (V)
   static __device__ __forceinline__ int swz(int part, int t) {
-    return (CH == 16 ? t << part : t) & (CH - 1);
+    if (CH != 16) return t & (CH - 1);
+    return part == 0 ? (t & 15) : (((t & 3) << 2) | ((t >> 1) & 2));
   }
   static __device__ __forceinline__ int off(int part, int t, int c) {
     return part * PART + t * ROW + ((c ^ swz(part, t)) << 4);
@@ -1051,9 +1057,9 @@ __device__ __forceinline__ void wide_init(WideState<D>& W, const PartialArgs& a,
 }
 
 // One 32-token tile of a 32-row tile, operands from an LDS stage (LdsTile
-// layout: K chunk c of token t at c ^ t, V chunk c at c ^ 2t, both mod 16 at
-// D = 128; the K reads of 8 consecutive tokens and the transpose reads of 4
-// tokens x 2 chunks then fall on distinct banks).
+// layout: K chunk c of token t at c ^ t, V chunk c at c ^ sv(t), both mod 16
+// at D = 128; the K reads of 8 consecutive tokens and each half wave's
+// transpose reads of 4 tokens x 4 chunks then fall on distinct banks).
 template <int D>
 __device__ __forceinline__ void wide_tile(WideState<D>& W, const char* stage, const PartialArgs& a,
                                           const WorkItem& it, int base) {
