@@ -208,6 +208,42 @@ def _ablation(args, inst, q, ks, vs, dev):
                       "variants": res}), flush=True)
 
 
+def _speculative(args, base, dev):
+    """The headline tree as a speculative-decoding verification step: the
+    last Q tokens of every leaf are queries (Q draft tokens per branch under
+    the leaf-local causal mask), with the same tree, heads and layout; timed
+    like the headline (same steps and warm-up) beside the headline's own
+    queries per leaf. Each leaf must hold at least Q tokens."""
+    import numpy as np
+
+    import synth
+    res = {}
+    for qpl in dict.fromkeys((base.qpl, args.speculative)):
+        if qpl != base.qpl:
+            has_child = np.zeros(base.n_nodes, bool)
+            has_child[base.parent[base.parent >= 0]] = True
+            shortest = int(base.node_len[~has_child].min())
+            if shortest < qpl:
+                raise SystemExit(f"--speculative {qpl}: the shortest leaf holds {shortest} tokens")
+            inst = synth.make_tree(base.parent, base.node_len, page_size=base.page_size, qpl=qpl,
+                                   n_qheads=base.n_qheads, n_kvheads=base.n_kvheads, head_dim=base.head_dim,
+                                   dtype=base.dtype, seed=synth.TREE_SEED_BASE + args.config,
+                                   name=f"{base.name}_qpl{qpl}")
+            synth.fill_tensors(inst, synth.TENSOR_SEED_BASE + args.config)
+        else:
+            inst = base
+        w = _prepare(inst, _copies(inst, args.copies), dev)
+        us, part, red, _, _ = _measure(inst, w["plan"], w["calls"], args.steps, args.warmup)
+        r = dict(_workload_desc(inst, w["copies"]), **_rates(inst, us, part, red))
+        r["query_tokens_per_s"] = round(inst.n_queries / (us * 1e-6), 1)
+        r["plan"] = _plan_info(w["plan"], inst)
+        w["plan"].close()
+        w.clear()
+        res[f"qpl_{qpl}"] = r
+    print(json.dumps({"speculative": base.name, "steps": args.steps, "warmup": args.warmup, "variants": res}),
+          flush=True)
+
+
 def _decode_loop(args, inst, dev):
     """Decode-loop plan reuse: W + K steps in which every leaf gains its
     queries' worth of tokens (tree_attn_plan_extend, pages handed out from
@@ -482,6 +518,9 @@ def main():
                     help="time the plan variants (greedy / all-0 / all-1 / no split) instead")
     ap.add_argument("--decode-loop", action="store_true",
                     help="time decode steps with plan reuse (every leaf grows each step) instead")
+    ap.add_argument("--speculative", type=int, default=0, metavar="Q",
+                    help="time the workload's tree with Q query tokens per leaf (a speculative verification "
+                         "step) beside its own queries per leaf, instead")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -506,6 +545,10 @@ def main():
 
     if args.decode_loop:
         _decode_loop(args, inst, dev)
+        return
+
+    if args.speculative:
+        _speculative(args, inst, dev)
         return
 
     if args.ablation:
