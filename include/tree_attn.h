@@ -21,7 +21,9 @@
  * KV chunk, kv-head) work item, which streams each chunk's paged KV from HBM
  * once for all the queries of the group, and one log-sum-exp reduction that
  * merges each query's partials along its path (DeFT notes, "tree-topology-aware
- * global reduction").
+ * global reduction"). A query whose path is one partial (one group, one chunk)
+ * gets its output from the partial-attention launch directly; when every
+ * query is such, the reduction is not enqueued.
  *
  * Conventions (all calls):
  *  - Every call returns a ta_status; on failure tree_attn_last_error() gives a
@@ -229,8 +231,9 @@ ta_status tree_attn_plan_export(const ta_plan* plan, int32_t table_id, int32_t* 
  * decode that is being captured into a graph.
  * tree_attn_timing_read() waits for the recorded events and writes per-decode
  * milliseconds of the partial-attention kernel (partial_ms[x]) and of the
- * reduction kernel (reduce_ms[x]); either pointer may be NULL. *n gets the
- * count and the record is cleared. */
+ * reduction kernel (reduce_ms[x]: 0 for a decode that launched none, every
+ * query having one partial); either pointer may be NULL. *n gets the count
+ * and the record is cleared. */
 ta_status tree_attn_timing_enable(ta_plan* plan, int32_t capacity);
 ta_status tree_attn_timing_read(ta_plan* plan, float* partial_ms, float* reduce_ms, int32_t* n);
 

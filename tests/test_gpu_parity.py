@@ -173,6 +173,41 @@ def test_speculative_trees(qpl, dtype):
     _check(_run(inst, force_edges=[1] * inst.n_nodes), ref, f"qpl {qpl} {dtype} all-1")
 
 
+@pytest.mark.parametrize("dtype,d,qpl", [(torch.bfloat16, 128, 4), (torch.bfloat16, 128, 32),
+                                         (torch.bfloat16, 64, 32), (torch.float32, 128, 4)])
+def test_single_slot_queries(dtype, d, qpl):
+    """A query whose path is one partial (one group, one chunk) takes its
+    output straight from the partial kernel, which normalises it; the
+    reduction skips it, and is not launched when every query is such. Every
+    edge joined without the split: one slot per query (no reduction launch);
+    one leaf joined to the root and one not: single-slot and two-slot queries
+    in one decode. Leaf groups of 16 rows (qpl 4) and of 128 rows (32-row
+    tiles), and the fp32 path."""
+    par, lens = [-1, 0, 0, 1], [300, 70, 90, 40]
+    inst = synth.make_tree(par, lens, page_size=16, qpl=qpl, n_qheads=8, n_kvheads=2, head_dim=d, dtype=dtype,
+                           seed=11)
+    synth.fill_tensors(inst, seed=12)
+    ref = ta.decode_instance(inst)
+    devt = _dev(inst)
+    tag = f"{str(dtype)[6:]} d{d} qpl{qpl}"
+    plan = Plan.for_instance(inst, force_edges=[1, 1, 1, 1], split=False, poison_workspace=True)
+    slots = np.diff(plan.export("q_slot_ptr"))
+    assert (slots == 1).all()
+    plan.timing_enable(2)  # the record stays whole without a reduction launch
+    out = plan.decode(*devt)
+    torch.cuda.synchronize()
+    pm, rm = plan.timing_read(2)
+    assert len(pm) == 1 and len(rm) == 1 and pm[0] > 0 and rm[0] == 0  # no reduction kernel
+    _check(out.cpu().numpy().astype(np.float64), ref, f"single-slot queries, every edge joined, {tag}")
+    plan.close()
+    kw = dict(force_edges=[0, 1, 0, 1], split=False)
+    plan = Plan.for_instance(inst, **kw)
+    slots = np.diff(plan.export("q_slot_ptr"))
+    assert (slots == 1).any() and (slots > 1).any()
+    plan.close()
+    _check(_run(inst, devt, **kw), ref, f"single- and two-slot queries, {tag}")
+
+
 def test_max_rows_per_item():
     """A group with many rows (root of 300 queries x GQA 8 = 2400 rows) spans
     several row blocks."""

@@ -97,6 +97,7 @@ struct ta_plan {
   bool sized_for_growth = false;  // the first extend gave every region and the workspace headroom
   // 4 per timed decode: start/stop of the partial kernel and of the reduction
   std::vector<hipEvent_t> ev;
+  std::vector<uint8_t> ev_reduced;  // per timed decode: 1 if it launched the reduction
   int32_t timing_cap = 0, timing_n = 0;
   // false after a device update failed part-way (the device tables or the
   // workspace may be gone): decode refuses the plan from then on
@@ -191,13 +192,14 @@ void device_forms(ta_plan* p) {
   }
   // per slot: workspace index of its q-head 0 and the q-head stride, pair-major
   // (the slots of one (query, q-head) adjacent, so the reduction reads them in
-  // one run)
+  // one run); a query's only slot holds -(q * n_qheads) - 1 and -1, so its rows
+  // find a negative index and write the query's output directly
   p->h_slot_pos.assign(2 * T.q_slots.size(), 0);
   for (int32_t q = 0; q < T.n_queries; ++q) {
     const int32_t s0 = T.q_slot_ptr[q], nsl = T.q_slot_ptr[q + 1] - s0;
     for (int32_t k = s0; k < s0 + nsl; ++k) {
-      p->h_slot_pos[2 * size_t(T.q_slots[k])] = s0 * p->n_qheads + (k - s0);
-      p->h_slot_pos[2 * size_t(T.q_slots[k]) + 1] = nsl;
+      p->h_slot_pos[2 * size_t(T.q_slots[k])] = nsl == 1 ? -(q * p->n_qheads) - 1 : s0 * p->n_qheads + (k - s0);
+      p->h_slot_pos[2 * size_t(T.q_slots[k]) + 1] = nsl == 1 ? -1 : nsl;
     }
   }
 }
@@ -573,6 +575,7 @@ ta_status decode_impl(const char* fn_name, const void* q, ta_dtype q_dtype, cons
   a.o_part = o_part;
   a.m_part = m_part;
   a.l_part = l_part;
+  a.out = out;
   a.n_qheads = plan->n_qheads;
   a.n_kvheads = plan->n_kvheads;
   a.g = plan->g;
@@ -591,8 +594,12 @@ ta_status decode_impl(const char* fn_name, const void* q, ta_dtype q_dtype, cons
   r.n_queries = plan->T.n_queries;
   r.n_qheads = plan->n_qheads;
   r.max_slots = plan->max_slots;
-  e = ta::launch_reduce(r, plan->head_dim, s, t_red);
-  if (e != hipSuccess) return hip_err(e, fn + ": reduction launch");
+  // with one slot per query the partial kernel wrote every output
+  if (plan->max_slots > 1) {
+    e = ta::launch_reduce(r, plan->head_dim, s, t_red);
+    if (e != hipSuccess) return hip_err(e, fn + ": reduction launch");
+  }
+  if (timed) mp->ev_reduced[size_t(mp->timing_n)] = plan->max_slots > 1 ? 1 : 0;
   if (timed) ++mp->timing_n;
   return TA_OK;
 }
@@ -833,6 +840,7 @@ ta_status tree_attn_timing_enable(ta_plan* plan, int32_t capacity) {
   plan->timing_n = 0;
   try {
     plan->ev.resize(size_t(capacity) * 4);
+    plan->ev_reduced.assign(size_t(capacity), 0);
   } catch (const std::bad_alloc&) {
     return set_err(TA_ENOMEM, "tree_attn_timing_enable: host allocation failed");
   }
@@ -853,12 +861,13 @@ ta_status tree_attn_timing_read(ta_plan* plan, float* partial_ms, float* reduce_
   const int32_t cnt = plan->timing_n;
   for (int32_t x = 0; x < cnt; ++x) {
     const hipEvent_t* ev = &plan->ev[4 * size_t(x)];
-    hipError_t e = hipEventSynchronize(ev[3]);
-    if (e == hipSuccess) e = hipEventSynchronize(ev[1]);
+    const bool reduced = plan->ev_reduced[size_t(x)] != 0;  // else no reduction kernel ran: 0 ms
+    hipError_t e = hipEventSynchronize(ev[1]);
+    if (e == hipSuccess && reduced) e = hipEventSynchronize(ev[3]);
     if (e != hipSuccess) return hip_err(e, "tree_attn_timing_read: hipEventSynchronize");
     float t0 = 0.0f, t1 = 0.0f;
     if ((e = hipEventElapsedTime(&t0, ev[0], ev[1])) != hipSuccess ||
-        (e = hipEventElapsedTime(&t1, ev[2], ev[3])) != hipSuccess)
+        (reduced && (e = hipEventElapsedTime(&t1, ev[2], ev[3])) != hipSuccess))
       return hip_err(e, "tree_attn_timing_read: hipEventElapsedTime");
     if (partial_ms) partial_ms[x] = t0;
     if (reduce_ms) reduce_ms[x] = t1;

@@ -35,7 +35,9 @@ struct PartialArgs {
   const int32_t* slot_pos; // per partial slot two words: the workspace index of its q-head 0 and
                            // the stride between q-heads. Pair-major: the slots of one (query q,
                            // q-head h), in path order, are adjacent, at s0 * n_qheads + h * nsl +
-                           // [0, nsl) with s0 = q_slot_ptr[q], nsl = q_slot_ptr[q + 1] - s0
+                           // [0, nsl) with s0 = q_slot_ptr[q], nsl = q_slot_ptr[q + 1] - s0; a
+                           // query's only slot (nsl = 1) holds -(q * n_qheads) - 1 and -1 instead
+                           // (its rows write the output directly, see out)
   const void* q;
   const void* k;
   const void* v;
@@ -47,6 +49,9 @@ struct PartialArgs {
                    // (every |o| below l) o / l as D fp16 values in the record's first half
   float* m_part;   // [n_slots (by position), n_qheads] running max, base-2 scaled units
   float* l_part;   // [n_slots (by position), n_qheads] sum of exp2(s - m), negated for fp16 records
+  float* out;      // [n_q, n_qheads, D]: rows of a query with a single partial slot (slot_pos holds
+                   // -(q * n_qheads) - 1 and -1 for its slot, so the row's index is negative) write
+                   // their normalised output here instead of a record
   int32_t n_qheads, n_kvheads, g;
   float scale_log2;  // softmax scale * log2(e)
 };

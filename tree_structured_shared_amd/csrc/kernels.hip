@@ -12,7 +12,9 @@
 // first half of the row's record with l stored negated (the reduction reads
 // the sign). The fp16 form rounds each value by at most 2^-12, a convex
 // combination of them moves the output by no more, and it halves the
-// partial results written and read back.
+// partial results written and read back. A query whose path is one partial
+// (one group, one chunk) needs no merge: its rows write the normalised
+// output directly and the reduction skips it.
 //
 // One launch (partial_kernel) holds both item classes, chosen per group by
 // its row count (the review's multi-stage query tiling: small tiles near the
@@ -163,8 +165,10 @@ __device__ __forceinline__ float part_weight(float m, float M) {
 // query qig, q-head-in-group hig); its partial goes to slot slot0 + qig, stored
 // at that slot's workspace index for the row's q-head (pair-major layout):
 // pi = slot_pos[2 s] + qh * slot_pos[2 s + 1], below 2^31 (the host checks
-// slots x q-heads against it). Only vis, pi and ok stay live over the tile
-// loop; gq and qh serve the Q load.
+// slots x q-heads against it). The only slot of a query q holds -(q *
+// n_qheads) - 1 and -1, so pi = -(q * n_qheads + qh) - 1 < 0: such rows write
+// their normalised output to out[-pi - 1] and no record. Only vis, pi and ok
+// stay live over the tile loop; gq and qh serve the Q load.
 struct RowRef {
   int gq, vis, qh, pi;
   bool ok;
@@ -377,12 +381,15 @@ __device__ __forceinline__ void valu_write(const ValuState<T, D, R>& S, const Pa
     int32_t pi32 = S.row[r].pi;
     asm volatile("" : "+v"(pi32));  // keep the 32-bit index live over the loop, widen here
     const int64_t pi = pi32;
-    float* op = a.o_part + pi * D + lane * EPL;
+    // a query with one partial: its normalised output, no record
+    const bool direct = pi < 0;
+    const float sc = direct ? 1.0f / S.l[r] : 1.0f;
+    float* op = (direct ? a.out + (-pi - 1) * D : a.o_part + pi * D) + lane * EPL;
 #pragma unroll
     for (int k4 = 0; k4 < EPL / 4; ++k4)
-      *reinterpret_cast<f32x4*>(op + 4 * k4) =
-          f32x4{S.o[r][4 * k4], S.o[r][4 * k4 + 1], S.o[r][4 * k4 + 2], S.o[r][4 * k4 + 3]};
-    if (lane == 0) {
+      *reinterpret_cast<f32x4*>(op + 4 * k4) = f32x4{S.o[r][4 * k4] * sc, S.o[r][4 * k4 + 1] * sc,
+                                                     S.o[r][4 * k4 + 2] * sc, S.o[r][4 * k4 + 3] * sc};
+    if (lane == 0 && !direct) {
       a.m_part[pi] = S.m[r];
       a.l_part[pi] = S.l[r];
     }
@@ -719,7 +726,11 @@ __device__ __forceinline__ void mfma_write(MfmaState<D, NRTW>& S, const PartialA
     int32_t pi32 = S.row[k].pi;
     asm volatile("" : "+v"(pi32));  // keep the 32-bit index live over the loop, widen here
     const int64_t pi = pi32;
-    if (half) {
+    // a query with one partial: its normalised output in fp32, no record
+    const bool direct = pi < 0;
+    const float sc = direct ? 1.0f / l : 1.0f;
+    float* const rec = direct ? a.out + (-pi - 1) * D : a.o_part + pi * D;
+    if (half && !direct) {
       const float inv = 1.0f / l;
       if constexpr (TR) {
         // lane j holds the 4-runs d = 16 db + 4 j; lanes j and j ^ 1 (l ^ 16)
@@ -764,23 +775,23 @@ __device__ __forceinline__ void mfma_write(MfmaState<D, NRTW>& S, const PartialA
         }
       }
     } else if constexpr (TR) {
-      float* op = a.o_part + pi * D + 4 * j;
+      float* op = rec + 4 * j;
 #pragma unroll
-      for (int db = 0; db < DPL; ++db) *reinterpret_cast<f32x4*>(op + 16 * db) = S.O[k][db];
+      for (int db = 0; db < DPL; ++db) *reinterpret_cast<f32x4*>(op + 16 * db) = S.O[k][db] * sc;
     } else {
-      float* op = a.o_part + pi * D + 4 * j * DPL;
+      float* op = rec + 4 * j * DPL;
 #pragma unroll
       for (int x4 = 0; x4 < DPL; ++x4) {
         f32x4 v;
 #pragma unroll
         for (int y = 0; y < 4; ++y) {
           const int x = 4 * x4 + y;  // local offset = c * DPL + db
-          v[y] = S.O[k][x % DPL][x / DPL];
+          v[y] = S.O[k][x % DPL][x / DPL] * sc;
         }
         *reinterpret_cast<f32x4*>(op + 4 * x4) = v;
       }
     }
-    if (j == 0) {
+    if (j == 0 && !direct) {
       a.m_part[pi] = S.m[k];
       a.l_part[pi] = half ? -l : l;
     }
@@ -1183,7 +1194,9 @@ __device__ __forceinline__ void wide_write(const WideState<D>& W, const PartialA
   int32_t pi32 = W.row.pi;
   asm volatile("" : "+v"(pi32));
   const int64_t pi = pi32;
-  if (half) {
+  // a query with one partial: its normalised output in fp32, no record
+  const bool direct = pi < 0;
+  if (half && !direct) {
     // lane h holds the 4-runs d = 32 db + 8 u + 4 h; for each pair of runs u
     // = 2 p, 2 p + 1 the lanes trade one run over permlane32, so lane h = 0
     // stores d = 32 db + 16 p + [0, 8) and lane h = 1 the next 8, each as one
@@ -1217,15 +1230,16 @@ __device__ __forceinline__ void wide_write(const WideState<D>& W, const PartialA
         *reinterpret_cast<u32x4*>(hp + 32 * db + 16 * pp) = out;
       }
   } else {
-    float* op = a.o_part + pi * D + 4 * h;
+    const float sc = direct ? 1.0f / l : 1.0f;
+    float* op = (direct ? a.out + (-pi - 1) * D : a.o_part + pi * D) + 4 * h;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        *reinterpret_cast<f32x4*>(op + 32 * db + 8 * u) =
-            f32x4{W.O[db][4 * u], W.O[db][4 * u + 1], W.O[db][4 * u + 2], W.O[db][4 * u + 3]};
+        *reinterpret_cast<f32x4*>(op + 32 * db + 8 * u) = f32x4{W.O[db][4 * u] * sc, W.O[db][4 * u + 1] * sc,
+                                                                 W.O[db][4 * u + 2] * sc, W.O[db][4 * u + 3] * sc};
   }
-  if (h == 0) {
+  if (h == 0 && !direct) {
     a.m_part[pi] = W.m;
     a.l_part[pi] = half ? -l : l;
   }
@@ -1483,6 +1497,9 @@ __global__ __launch_bounds__(kBlock) void lse_reduce_kernel(ReduceArgs a) {
     s0 = __builtin_amdgcn_readfirstlane(s0);
     s1 = __builtin_amdgcn_readfirstlane(s1);
   }
+  // a query with a single slot has its output written by the partial kernel
+  const bool single = s1 - s0 == 1;
+  if (single) s1 = s0;
   float M = TA_NEG_INF, L = 0.0f;
   float acc[EPL];
 #pragma unroll
@@ -1546,7 +1563,7 @@ __global__ __launch_bounds__(kBlock) void lse_reduce_kernel(ReduceArgs a) {
     }
     M = Mn;
   }
-  if (sg == 0 && live) {
+  if (sg == 0 && live && !single) {
     const float inv = 1.0f / L;
     float* op = a.out + (int64_t(q) * a.n_qheads + hq) * D + sub * EPL;
 #pragma unroll
