@@ -45,6 +45,37 @@ def test_extend_decode_matches_oracle(dtype, qpl):
     plan.close()
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_extend_across_single_slot_queries(dtype):
+    """Every edge joined on a small tree: each leaf's group is its whole path
+    in one chunk, so every query has one slot (outputs written by the partial
+    kernel, no reduction launch). Growing one leaf past the chunk length
+    gives its queries several slots while the other leaf's keep one (mixed),
+    then both: the slot table moves from the direct form to the partial
+    records in place, and the reduction comes back."""
+    par, lens = [-1, 0, 0], [50, 30, 40]
+    inst = synth.make_tree(par, lens, page_size=16, qpl=2, n_qheads=16, n_kvheads=4, head_dim=128, dtype=dtype,
+                           seed=5)
+    inst = synth.fill_tensors(inst, seed=6)
+    plan = Plan.for_instance(inst, poison_workspace=True, force_edges=[1, 1, 1])
+    slots = np.diff(plan.export("q_slot_ptr"))
+    assert (slots == 1).all()
+    out = plan.decode(inst.q.cuda(), inst.k_pool.cuda(), inst.v_pool.cuda())
+    _check(out, ta.decode_instance(inst), f"{dtype} one slot per query")
+    for step, add in enumerate(([300, 2], [2, 300], [2, 2])):
+        add = np.asarray(add, np.int64)
+        inst, new_pages = synth.grow_leaves(inst, add, seed=50 + step)
+        plan.extend(add, new_pages)
+        slots = np.diff(plan.export("q_slot_ptr"))
+        out = plan.decode(inst.q.cuda(), inst.k_pool.cuda(), inst.v_pool.cuda())
+        _check(out, ta.decode_instance(inst), f"{dtype} step {step} slots per query {slots.tolist()}")
+        if step == 0:
+            assert (slots == 1).any() and (slots > 1).any()
+        if step == 2:
+            assert (slots > 1).all()
+    plan.close()
+
+
 def test_extend_config2_decode_loop():
     """The multi-level prompt workload, one token per leaf per step."""
     inst = synth.make_config(2)
