@@ -57,7 +57,8 @@ struct PartialArgs {
 };
 
 struct ReduceArgs {
-  const int32_t* q_slot_ptr;  // query q holds slots [q_slot_ptr[q], q_slot_ptr[q + 1]) (pair-major workspace)
+  const int32_t* q_slot_ptr;  // query q holds slots [q_slot_ptr[q], q_slot_ptr[q + 1]) (pair-major workspace);
+                              // a query with one slot is skipped (the partial kernel wrote its output)
   const float* o_part;  // records as the partial kernel writes them (fp32 o, or fp16 o / l)
   const float* m_part;
   const float* l_part;  // negative (or -0) for an fp16 record
