@@ -27,10 +27,10 @@ def _decode(fn, plan, q, k, v, out):
               ctypes.c_void_p(stream))
 
 
-def _case(inst, what):
+def _case(inst, what, **plan_kw):
     L = _capi.lib()
     q, k, v = inst.q.cuda(), inst.k_pool.cuda(), inst.v_pool.cuda()
-    plan = Plan.for_instance(inst, poison_workspace=True)
+    plan = Plan.for_instance(inst, poison_workspace=True, **plan_kw)
     ref_out = torch.empty((inst.n_queries, inst.n_qheads, inst.head_dim), dtype=torch.float32, device="cuda")
     got = torch.empty_like(ref_out)
     assert _decode(L.tree_attn_decode, plan, q, k, v, ref_out) == _capi.TA_OK
@@ -44,12 +44,15 @@ def _case(inst, what):
 
 
 def test_noalloc_matches_decode_twice_smaller_second():
-    big = synth.make_config(5)                      # 38 MB of partials: most of the scratch
+    big = synth.make_config(5)                      # 28 MB of partials: over half the scratch
     _case(big, "random radix tree")
     small = synth.make_tree([-1, 0, 0, 1], [300, 40, 70, 9], page_size=16, qpl=2, n_qheads=16, n_kvheads=2,
                             head_dim=128, seed=1)
     synth.fill_tensors(small, seed=2)
     _case(small, "small tree after the large one")
+    # every edge joined, no split: one slot per query, outputs straight from
+    # the partial kernel and no reduction launch
+    _case(small, "small tree, one slot per query", force_edges=[1, 1, 1, 1], split=False)
 
 
 def test_noalloc_refuses_a_workspace_beyond_the_scratch():
