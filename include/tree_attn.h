@@ -16,7 +16,7 @@
  * padding and intermediate-result cost model) turns the tree into KV-guided
  * context-query groups (DeFT notes, "KV-guided tree split"), long groups are
  * cut into KV chunks (FastTree review, section 3.3), and the resulting tables
- * are uploaded once. tree_attn_decode() then enqueues two HIP kernels on the
+ * are uploaded once. tree_attn_decode() then enqueues (up to) two HIP kernels on the
  * caller's stream: one partial-attention launch over every (group, row block,
  * KV chunk, kv-head) work item, which streams each chunk's paged KV from HBM
  * once for all the queries of the group, and one log-sum-exp reduction that
@@ -225,7 +225,7 @@ ta_status tree_attn_plan_export(const ta_plan* plan, int32_t table_id, int32_t* 
 
 /* Timing of the last decodes (testing and benchmarking). After
  * tree_attn_timing_enable(plan, capacity) every decode, for up to `capacity`
- * decodes, launches its two kernels with HIP start/stop events that the
+ * decodes, launches its kernels with HIP start/stop events that the
  * runtime stamps at the start and at the end of each kernel's own execution
  * (not at enqueue); capacity 0 turns timing off. Do not enable timing on a
  * decode that is being captured into a graph.
